@@ -1,0 +1,180 @@
+"""fp64 per-document causal softmax attention, forward and backward.
+
+Test infrastructure only (see ``oracle/__init__``).
+
+What is computed (the plain definition; no tiling, no online softmax):
+  For every segment [s, e) of ``cu_seqlens`` (a padding tail is a segment like
+  any other), every query head h and its key/value head g = h // G with
+  G = Hq / Hkv:
+    S_ij  = scale * <q_i, k_j>            for s <= j <= i < e
+    lse_i = log sum_j exp(S_ij)           (natural log)
+    P_ij  = exp(S_ij - lse_i)
+    o_i   = sum_j P_ij v_j
+  Backward, for an upstream gradient dO:
+    dP_ij = <dO_i, v_j>,   D_i = sum_j P_ij dP_ij  (= <dO_i, o_i>)
+    dS_ij = P_ij (dP_ij - D_i)
+    dq_i  = scale * sum_j dS_ij k_j
+    dk_j  = scale * sum_i dS_ij q_i   (summed over the G query heads of g)
+    dv_j  = sum_i P_ij dO_i           (summed over the G query heads of g)
+
+Sources:
+  * "Sample Packing：长序列 LLM 训练的 Attention 问题及优化", section 三
+    (Attention Mask): the block-diagonal mask is one lower-triangular causal
+    block per document (diagonal included), and packed attention is the same as
+    running each document on its own;
+  * InternEvo "数据加载与流程", section "ISP并行模式下数据流程" (qkv split and
+    attention): the grouped qkv layout, where the first G slots of each
+    key/value head's group are its query heads, so query head h reads
+    key/value head h // G;
+  * softmax scale 1/sqrt(D) unless given (the pages do not fix it).
+
+Inputs of any float dtype are converted exactly to fp64 first, so the oracle
+sees the same quantised values as a bf16 kernel.  Query rows are processed in
+blocks of at most ``block`` rows so one long document never needs its full
+L x L score matrix.
+
+Pins: tests/test_oracle_attn.py (dense Megatron-mask brute force, per-document
+torch SDPA + autograd in fp64, closed forms, central finite differences, the
+packed == documents-alone invariant).
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+
+def _f64(x):
+    try:
+        import torch
+
+        if isinstance(x, torch.Tensor):
+            return x.detach().to("cpu", torch.float64).numpy()
+    except ImportError:  # pragma: no cover
+        pass
+    return np.asarray(x, dtype=np.float64)
+
+
+def _segments(cu_seqlens):
+    cu = [int(c) for c in np.asarray(cu_seqlens).reshape(-1)]
+    return [(cu[i], cu[i + 1]) for i in range(len(cu) - 1) if cu[i + 1] > cu[i]]
+
+
+def _scale(head_dim, softmax_scale):
+    return 1.0 / math.sqrt(head_dim) if softmax_scale is None else float(softmax_scale)
+
+
+def _causal_block_scores(Qb, Kpre, i0, scale):
+    """Scores of query rows i0.. (segment-local) against keys 0..i1-1, with the
+    entries j > i set to -inf."""
+    b = Qb.shape[0]
+    S = scale * (Qb @ Kpre.T)
+    rows = i0 + np.arange(b)[:, None]
+    cols = np.arange(Kpre.shape[0])[None, :]
+    S[cols > rows] = -np.inf
+    return S
+
+
+def attn_fwd(q, k, v, cu_seqlens, softmax_scale=None, block=512):
+    """Returns (o [T,Hq,D] fp64, lse [Hq,T] fp64)."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    T, Hq, D = q.shape
+    Hkv = k.shape[1]
+    assert Hq % Hkv == 0
+    G = Hq // Hkv
+    scale = _scale(D, softmax_scale)
+    o = np.zeros_like(q)
+    lse = np.zeros((Hq, T))
+    for s, e in _segments(cu_seqlens):
+        L = e - s
+        for h in range(Hq):
+            g = h // G
+            Q, K, V = q[s:e, h], k[s:e, g], v[s:e, g]
+            for i0 in range(0, L, block):
+                i1 = min(i0 + block, L)
+                S = _causal_block_scores(Q[i0:i1], K[:i1], i0, scale)
+                m = S.max(axis=1, keepdims=True)
+                l = np.log(np.exp(S - m).sum(axis=1, keepdims=True)) + m
+                P = np.exp(S - l)
+                o[s + i0:s + i1, h] = P @ V[:i1]
+                lse[h, s + i0:s + i1] = l[:, 0]
+    return o, lse
+
+
+def attn_bwd(q, k, v, do, cu_seqlens, softmax_scale=None, block=512):
+    """Gradients of sum(dO * o) w.r.t. q, k, v.  Returns (dq, dk, dv) fp64."""
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    T, Hq, D = q.shape
+    Hkv = k.shape[1]
+    G = Hq // Hkv
+    scale = _scale(D, softmax_scale)
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for s, e in _segments(cu_seqlens):
+        L = e - s
+        for h in range(Hq):
+            g = h // G
+            Q, K, V, dO = q[s:e, h], k[s:e, g], v[s:e, g], do[s:e, h]
+            for i0 in range(0, L, block):
+                i1 = min(i0 + block, L)
+                S = _causal_block_scores(Q[i0:i1], K[:i1], i0, scale)
+                m = S.max(axis=1, keepdims=True)
+                P = np.exp(S - m)
+                P /= P.sum(axis=1, keepdims=True)
+                dP = dO[i0:i1] @ V[:i1].T
+                Drow = (P * dP).sum(axis=1, keepdims=True)
+                dS = P * (dP - Drow)
+                dq[s + i0:s + i1, h] = scale * (dS @ K[:i1])
+                dk[s:s + i1, g] += scale * (dS.T @ Q[i0:i1])
+                dv[s:s + i1, g] += P.T @ dO[i0:i1]
+    return dq, dk, dv
+
+
+def attn_rows(q, k, v, cu_seqlens, rows, heads, softmax_scale=None):
+    """Forward outputs and dq for selected (token, head) pairs only, each from
+    its own segment prefix; cheap spot checks at full size.
+
+    Returns o [n, D], lse [n]; when ``do`` style checks are needed use
+    ``attn_rows_bwd``.
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    D = q.shape[2]
+    G = q.shape[1] // k.shape[1]
+    scale = _scale(D, softmax_scale)
+    cu = np.asarray(cu_seqlens).reshape(-1).astype(np.int64)
+    outs, lses = [], []
+    for t, h in zip(rows, heads):
+        sidx = int(np.searchsorted(cu, t, side="right")) - 1
+        s = int(cu[sidx])
+        g = h // G
+        srow = scale * (k[s:t + 1, g] @ q[t, h])
+        m = srow.max()
+        l = m + math.log(np.exp(srow - m).sum())
+        p = np.exp(srow - l)
+        outs.append(p @ v[s:t + 1, g])
+        lses.append(l)
+    return np.array(outs), np.array(lses)
+
+
+def attn_rows_dq(q, k, v, do, cu_seqlens, rows, heads, softmax_scale=None):
+    """dq for selected (token, head) pairs; row t of dq depends only on row t's
+    scores, so each is computed alone."""
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    D = q.shape[2]
+    G = q.shape[1] // k.shape[1]
+    scale = _scale(D, softmax_scale)
+    cu = np.asarray(cu_seqlens).reshape(-1).astype(np.int64)
+    out = []
+    for t, h in zip(rows, heads):
+        sidx = int(np.searchsorted(cu, t, side="right")) - 1
+        s = int(cu[sidx])
+        g = h // G
+        K, V = k[s:t + 1, g], v[s:t + 1, g]
+        srow = scale * (K @ q[t, h])
+        p = np.exp(srow - srow.max())
+        p /= p.sum()
+        dp = V @ do[t, h]
+        ds = p * (dp - (p * dp).sum())
+        out.append(scale * (ds @ K))
+    return np.array(out)
