@@ -1,0 +1,246 @@
+#!/usr/bin/env python3
+"""Benchmark of the packing + document-causal attention path on one MI355X.
+
+One step = the whole path over one synthetic batch already resident in HBM:
+  1. GPU packing of the workload's document stream (psc_pack_build),
+  2. attention forward over the packed rows' segments (psc_varlen_attn_fwd),
+  3. attention backward (psc_varlen_attn_bwd), unless the workload is
+     forward-only.
+Throughput counts only in-document causal FLOPs: forward
+4 * D * Hq * sum over real segments of L(L+1)/2, backward 2.5x that (padding
+segments are computed but not counted).  The default workload is the
+2 x 32768-token log-normal pack with GQA 32/8 heads, head_dim 128, bf16.
+
+Prints one JSON line.  Besides the standard fields it carries
+  roofline:     the dominant kernel's algorithmic FLOP rate (HIP events
+                recorded by the library around that kernel on its stream,
+                summed over the timed steps) against the bf16 MFMA peak;
+  cpu_baseline: the fp64 CPU oracle timed on a bounded sample of the same
+                workload (whole documents in order until ~--cpu-seconds of
+                work), in the same unit.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "varlen causal attn fwd+bwd TFLOP/s (in-doc FLOPs) & % MFMA peak, 1 GPU"
+PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 4096 dense bf16 FLOP/clk x 2.4 GHz (published 2.5 PFLOP/s)
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="lognormal_32k")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the CPU oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def real_segments(w, cu):
+    """Boolean per segment: True for documents, False for padding tails."""
+    import numpy as np
+
+    if w.attn_is_pad is not None:
+        return ~np.asarray(w.attn_is_pad, dtype=bool)
+    return np.ones(len(cu) - 1, dtype=bool)
+
+
+def cpu_baseline(w, q, k, v, do, cu, real, budget_s):
+    """The oracle as it stands, on whole documents in order until the budget."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from oracle import attn_ref
+
+    a = w.attn
+    lens = np.diff(cu)
+    flops, docs, heads_done = 0.0, 0, 0
+    t0 = time.perf_counter()
+    for i in range(len(lens)):
+        if not real[i]:
+            continue
+        s, e = int(cu[i]), int(cu[i + 1])
+        one = np.array([0, e - s])
+        # one key/value group (its hq/hkv query heads) per document keeps the sample bounded
+        g = docs % a.hkv
+        G = a.hq // a.hkv
+        qs = q[s:e, g * G:(g + 1) * G]
+        ks, vs, dos = k[s:e, g:g + 1], v[s:e, g:g + 1], do[s:e, g * G:(g + 1) * G]
+        attn_ref.attn_fwd(qs, ks, vs, one)
+        mult = 1.0
+        if a.backward:
+            attn_ref.attn_bwd(qs, ks, vs, dos, one)
+            mult += 2.5
+        L = e - s
+        flops += mult * 4.0 * a.head_dim * G * L * (L + 1) / 2
+        docs += 1
+        heads_done += G
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    return {
+        "value": flops / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"fp64 NumPy oracle, fwd{'+bwd' if a.backward else ''} of the first {docs} documents "
+                  f"(one key/value group of {a.hq // a.hkv} query heads each), {flops:.3e} in-doc FLOP "
+                  f"in {dt:.1f} s",
+        "seconds": dt,
+    }
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import packed_sequence_causal_amd as psc
+    import workloads
+
+    dev = torch.device("cuda:0")
+    w = workloads.make(args.workload, args.seed)
+    a = w.attn
+    mode = psc.PACK if w.pack.mode == workloads.BUILD_PACK else psc.UNPACK
+
+    toks = torch.from_numpy(w.pack.tokens).to(dev)
+    offs = torch.from_numpy(w.pack.doc_offsets).to(dev)
+    pk = psc.pack_build(toks, offs, w.pack.micro_bsz, w.pack.seq_len, mode)
+    torch.cuda.synchronize()
+    if w.attn_cu_seqlens is None:
+        # attention runs on the first keep_rows rows of the packer's own output
+        n_seg = int(pk["row_seg_ptr"][w.pack.keep_rows].item())
+        cu = pk["cu_seqlens"][: n_seg + 1]
+    else:
+        cu = torch.from_numpy(np.asarray(w.attn_cu_seqlens, dtype=np.int32)).to(dev)
+        n_seg = cu.numel() - 1
+    cu_h = cu.cpu().numpy().astype(np.int64)
+    T = int(cu_h[-1])
+    lens = np.diff(cu_h)
+    max_seqlen = int(lens.max())
+    real = real_segments(w, cu_h)
+    pairs = float((lens[real] * (lens[real] + 1) // 2).sum())
+    real_tokens = int(lens[real].sum())
+    fwd_flops = 4.0 * a.head_dim * a.hq * pairs
+    bwd_flops = 2.5 * fwd_flops if a.backward else 0.0
+
+    q, k, v, do = workloads.qkv_do(T, a.hq, a.hkv, a.head_dim, seed=args.seed, dtype=a.dtype)
+    qd, kd, vd, dod = q.to(dev), k.to(dev), v.to(dev), do.to(dev)
+    o, lse = psc.varlen_attn_fwd(qd, kd, vd, cu, max_seqlen, n_segments=n_seg)
+    ws_f = torch.empty(psc.varlen_attn_workspace(0, psc.BF16 if a.dtype == "bf16" else psc.F32, T, n_seg,
+                                                 max_seqlen, a.hq, a.hkv, a.head_dim), dtype=torch.uint8,
+                       device=dev)
+    grads = ws_b = None
+    if a.backward:
+        grads = psc.varlen_attn_bwd(qd, kd, vd, o, dod, lse, cu, max_seqlen, n_segments=n_seg)
+        ws_b = torch.empty(psc.varlen_attn_workspace(1, psc.BF16 if a.dtype == "bf16" else psc.F32, T, n_seg,
+                                                     max_seqlen, a.hq, a.hkv, a.head_dim), dtype=torch.uint8,
+                           device=dev)
+    pk_ws = pk["_workspace"]
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+
+    def step(e=None):
+        if e:
+            e[0].record()
+        psc.pack_build(toks, offs, w.pack.micro_bsz, w.pack.seq_len, mode, out=pk, workspace=pk_ws)
+        if e:
+            e[1].record()
+        psc.varlen_attn_fwd(qd, kd, vd, cu, max_seqlen, n_segments=n_seg, out=o, lse=lse, workspace=ws_f)
+        if e:
+            e[2].record()
+        if a.backward:
+            psc.varlen_attn_bwd(qd, kd, vd, o, dod, lse, cu, max_seqlen, n_segments=n_seg, dq=grads[0],
+                                dk=grads[1], dv=grads[2], workspace=ws_b)
+        if e:
+            e[3].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    psc.timing_reset()
+    psc.timing_enable(True)
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for i in range(args.steps):
+        step(ev[i])
+    t1.record()
+    torch.cuda.synchronize()
+    psc.timing_enable(False)
+    kt = psc.timing_read()
+    ms = t0.elapsed_time(t1) / args.steps
+    pack_ms = float(np.median([e[0].elapsed_time(e[1]) for e in ev]))
+    fwd_ms = float(np.median([e[1].elapsed_time(e[2]) for e in ev]))
+    bwd_ms = float(np.median([e[2].elapsed_time(e[3]) for e in ev])) if a.backward else 0.0
+
+    total_flops = fwd_flops + bwd_flops
+    value = total_flops / (ms * 1e-3) / 1e12
+
+    # dominant kernel and its algorithmic work per launch: forward = the two
+    # in-document products; dK/dV = S, dP, dV, dK (2.0x forward); dQ = the dQ
+    # product only (0.5x forward; the S and dP it recomputes are counted once,
+    # in dK/dV), so the backward kernels sum to the 2.5x convention.
+    algo = {"attn_fwd": fwd_flops, "attn_bwd_dkdv": 2.0 * fwd_flops if a.backward else 0.0,
+            "attn_bwd_dq": 0.5 * fwd_flops if a.backward else 0.0}
+    dom = max(algo, key=lambda n: kt[n][0])
+    dom_ms, dom_n = kt[dom]
+    dom_avg = dom_ms / max(dom_n, 1)
+    achieved = algo[dom] / (dom_avg * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "avg_launch_ms": round(dom_avg, 4), "launches": dom_n}
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": a.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "tokens": T, "real_tokens": real_tokens, "segments": n_seg,
+                   "max_seqlen": max_seqlen, "hq": a.hq, "hkv": a.hkv, "head_dim": a.head_dim,
+                   "packer": f"{w.pack.mode}(micro_bsz={w.pack.micro_bsz}, seq_len={w.pack.seq_len}), "
+                             f"{len(w.pack.docs)} docs",
+                   "passes": "pack+fwd+bwd" if a.backward else "pack+fwd", "seed": args.seed},
+        "pct_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "tokens_per_s": round(real_tokens / (ms * 1e-3), 1),
+        "pack_ms": round(pack_ms, 4),
+        "fwd": {"ms": round(fwd_ms, 4), "tflops": round(fwd_flops / (fwd_ms * 1e-3) / 1e12, 2),
+                "pct_peak": round(100 * fwd_flops / (fwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2)},
+        "kernels_ms_per_step": {n: round(t / args.steps, 4) for n, (t, c) in kt.items() if c},
+        "roofline": roofline,
+    }
+    if a.backward:
+        result["bwd"] = {"ms": round(bwd_ms, 4), "tflops": round(bwd_flops / (bwd_ms * 1e-3) / 1e12, 2),
+                         "pct_peak": round(100 * bwd_flops / (bwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2)}
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, q, k, v, do, cu_h, real, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,220 @@
+/*
+ * psc.h — sample packing and document-causal ("varlen") attention on AMD
+ * Instinct MI355X (gfx950).  C ABI of libpsc.so.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Pointers are DEVICE pointers unless the comment says (host).
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Every
+ *    call that takes a stream only enqueues work on it and returns; outputs are
+ *    ready when the stream reaches that point.
+ *  - Return value: PSC_OK (0) or a negative psc_status.  Arguments are checked
+ *    on the host before anything is enqueued; on any error nothing is launched
+ *    and no output is touched.  A failed launch returns PSC_ERR_HIP.
+ *  - The library allocates no device memory.  The caller owns every buffer,
+ *    including the scratch `workspace`, whose size comes from the matching
+ *    *_workspace / *_sizes call.  No pointer is kept after a call returns.
+ *  - Calls are reentrant; two calls that share an output or a workspace buffer
+ *    must not overlap in time.
+ *  - No C++ exception crosses this interface.
+ *
+ * Source of the operations: the InternEvo documentation page
+ * "数据加载与流程" (data flow) defines packing, labels, cu_seqlens and indexes
+ * (sections "Dataloader加载数据", "获取Dataloader数据", "处理数据") and the
+ * grouped query/key/value head layout (section "ISP并行模式下数据流程");
+ * "Sample Packing：长序列 LLM 训练的 Attention 问题及优化" defines the
+ * block-diagonal causal mask (section 三) and the per-document decomposition
+ * used here (section 5.1).
+ */
+#ifndef PSC_H_
+#define PSC_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum psc_status {
+  PSC_OK = 0,
+  PSC_ERR_INVALID = -1,     /* bad argument: null pointer, size, stride, alignment */
+  PSC_ERR_UNSUPPORTED = -2, /* valid but not implemented (e.g. head_dim 96) */
+  PSC_ERR_WORKSPACE = -3,   /* workspace null or smaller than required */
+  PSC_ERR_CAPACITY = -4,    /* an output buffer capacity is too small */
+  PSC_ERR_HIP = -5          /* the HIP runtime reported an error at launch */
+} psc_status;
+
+typedef enum psc_pack_mode {
+  PSC_BUILD_PACK = 0,   /* carry-over packing (build_pack) */
+  PSC_BUILD_UNPACK = 1  /* truncate to SEQ_LEN, at most micro_bsz docs a row, zero pad (build_unpack) */
+} psc_pack_mode;
+
+typedef enum psc_dtype {
+  PSC_F32 = 0,
+  PSC_BF16 = 1
+} psc_dtype;
+
+/* Human-readable text for a status code (static storage). */
+const char* psc_strerror(int status);
+
+/* Library version, major*10000 + minor*100 + patch. */
+int psc_version(void);
+
+/* ------------------------------------------------------------------------ */
+/* Packing                                                                   */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * psc_pack_sizes — host-only sizing for psc_pack_build.
+ *
+ *   n_rows        (host out) rows to allocate: build_pack ceil(n_tokens / PL),
+ *                 build_unpack ceil(n_docs / micro_bsz), PL = micro_bsz*seq_len.
+ *   max_segments  (host out) capacity bound for cu_seqlens (which then needs
+ *                 max_segments + 1 entries): build_pack n_docs + 2*n_rows,
+ *                 build_unpack n_docs + n_rows.
+ *   workspace_bytes (host out) scratch needed by psc_pack_build.
+ * Errors: PSC_ERR_INVALID for an unknown mode, negative counts, micro_bsz or
+ * seq_len < 1, a packed length above 2^30, or a null output pointer.
+ */
+int psc_pack_sizes(int mode, int64_t n_docs, int64_t n_tokens, int32_t micro_bsz,
+                   int32_t seq_len, int64_t* n_rows, int64_t* max_segments,
+                   size_t* workspace_bytes);
+
+/*
+ * psc_pack_build — pack documents into rows of PL = micro_bsz*seq_len tokens.
+ *
+ * InternEvo "数据加载与流程", section "Dataloader加载数据":
+ *  - PSC_BUILD_PACK: documents are laid end to end and cut every PL tokens; a
+ *    document crossing a cut continues at the start of the next row; only the
+ *    last row is padded.
+ *  - PSC_BUILD_UNPACK: each document is cut to its first seq_len tokens, rows
+ *    take micro_bsz documents each in order, and are padded to PL.
+ * Labels: the next token of the same document, -100 on a document's last token
+ * and on padding (formed before a document is split across rows, after it is
+ * truncated).  Padding ids are 0.  Documents with no tokens are skipped.
+ * Segments (section "获取Dataloader数据"): each row is cut at its start, at
+ * every document start inside it, and at the start of its padding tail; the
+ * padding tail is a segment of its own.  indexes count from 0 in every segment.
+ *
+ * Inputs
+ *   tokens       int32 [n_tokens]           token ids, documents back to back
+ *   doc_offsets  int64 [n_docs + 1]         doc d = tokens[doc_offsets[d] .. doc_offsets[d+1]);
+ *                                           precondition: doc_offsets[0] == 0, non-decreasing,
+ *                                           doc_offsets[n_docs] == n_tokens.  Offsets outside
+ *                                           [0, n_tokens] are clamped, never dereferenced.
+ *   n_rows       must equal psc_pack_sizes' n_rows.
+ * Outputs (all written in full)
+ *   input_ids, labels, indexes  int32 [n_rows][PL]
+ *   cu_seqlens   int32 [max_segments + 1]   all rows' boundaries, flattened: row r's
+ *                                           boundary b is stored as r*PL + b, so the
+ *                                           array runs from 0 to rows_filled*PL.
+ *                                           Entries after index n_seg are not written.
+ *   row_seg_ptr  int32 [n_rows + 1]         row r's boundaries are
+ *                                           cu_seqlens[row_seg_ptr[r] .. row_seg_ptr[r+1]].
+ *   row_valid_len int32 [n_rows] or NULL    tokens before the row's padding.
+ *   stats        int32 [4]                  n_seg, max_seqlen (longest segment, padding
+ *                                           included), rows_filled, 0.
+ * Rows past rows_filled (only when build_unpack meets empty documents) hold
+ * padding only and no segment.
+ * Errors: PSC_ERR_INVALID (null pointer, sizes inconsistent with
+ * psc_pack_sizes), PSC_ERR_CAPACITY (max_segments too small),
+ * PSC_ERR_WORKSPACE, PSC_ERR_HIP.
+ */
+int psc_pack_build(int mode, const int32_t* tokens, const int64_t* doc_offsets,
+                   int64_t n_docs, int64_t n_tokens, int32_t micro_bsz, int32_t seq_len,
+                   int64_t n_rows, int32_t* input_ids, int32_t* labels, int32_t* indexes,
+                   int32_t* cu_seqlens, int64_t max_segments, int32_t* row_seg_ptr,
+                   int32_t* row_valid_len, int32_t* stats, void* workspace,
+                   size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Document-causal attention                                                 */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Shapes shared by the attention calls.  T = total_tokens (all rows laid end to
+ * end; a row end is always a segment end, so rows need no separate handling).
+ *   q   [T, hq,  D] ; k, v [T, hkv, D] ; out, dout [T, hq, D]
+ * Each is addressed as base + t*tok_stride + h*D + d (strides in elements), so
+ * q, k, v may be views into one packed qkv buffer.  tok_stride >= heads*D;
+ * for PSC_BF16, base and tok_stride*2 must be multiples of 16 bytes.
+ * cu_seqlens int32 [n_segments + 1]: 0 = c_0 < c_1 < ... < c_n = T (strictly
+ * increasing; precondition, not checked on the device).  max_seqlen >= the
+ * longest segment (used for scratch sizing only; never for addressing).
+ * Query head h reads key/value head h / (hq/hkv) (grouped-query attention:
+ * InternEvo "数据加载与流程", section "ISP并行模式下数据流程", qkv split).
+ * softmax_scale <= 0 selects 1/sqrt(D).
+ * head_dim: PSC_BF16 supports 64 and 128; PSC_F32 supports 32, 64, 128.
+ *
+ * Every token i of segment [s, e) attends to keys j with s <= j <= i and to
+ * nothing else (one causal triangle per document, "Sample Packing：长序列 LLM
+ * 训练的 Attention 问题及优化", section 三); no mask is ever stored and no tile
+ * outside the triangles is visited (section 5.1).
+ */
+
+/* psc_varlen_attn_workspace — scratch bytes for pass 0 (fwd) or 1 (bwd). */
+int psc_varlen_attn_workspace(int pass, int dtype, int64_t total_tokens, int32_t n_segments,
+                              int32_t max_seqlen, int32_t hq, int32_t hkv, int32_t head_dim,
+                              size_t* bytes /* host out */);
+
+/*
+ * psc_varlen_attn_fwd
+ *   out  [T, hq, D] in `dtype`, row stride out_tok_stride.
+ *   lse  float32 [hq, T]: natural-log log-sum-exp of the scaled scores of each
+ *        (head, token) over its causal prefix inside its document.
+ * Accumulation is fp32; PSC_BF16 multiplies in bf16 (Q K^T, and P V with P
+ * rounded to bf16), PSC_F32 entirely in fp32.
+ */
+int psc_varlen_attn_fwd(int dtype, const void* q, const void* k, const void* v,
+                        int64_t q_tok_stride, int64_t k_tok_stride, int64_t v_tok_stride,
+                        const int32_t* cu_seqlens, int32_t n_segments, int32_t max_seqlen,
+                        int64_t total_tokens, int32_t hq, int32_t hkv, int32_t head_dim,
+                        float softmax_scale, void* out, int64_t out_tok_stride, float* lse,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * psc_varlen_attn_bwd — gradients of sum(dout * out) for the forward above.
+ *   out, lse: the forward's outputs for the same inputs.
+ *   dq [T, hq, D], dk [T, hkv, D], dv [T, hkv, D]: float32, contiguous
+ *   (token stride heads*D).  dk and dv sum over the hq/hkv query heads of
+ *   each key/value head.  All three are written in full.
+ */
+int psc_varlen_attn_bwd(int dtype, const void* q, const void* k, const void* v,
+                        const void* out, const void* dout, const float* lse,
+                        int64_t q_tok_stride, int64_t k_tok_stride, int64_t v_tok_stride,
+                        int64_t out_tok_stride, int64_t dout_tok_stride,
+                        const int32_t* cu_seqlens, int32_t n_segments, int32_t max_seqlen,
+                        int64_t total_tokens, int32_t hq, int32_t hkv, int32_t head_dim,
+                        float softmax_scale, float* dq, float* dk, float* dv,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Instrumentation                                                           */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Kernel timing with HIP events.  While enabled, every launch of the kernels
+ * below is bracketed by two events recorded on the launch stream (the whole
+ * packer sequence counts as one "pack" launch).  psc_timing_read waits for the
+ * recorded events and returns the summed elapsed time and launch count since
+ * the last reset.  Host-side bookkeeping is thread safe; disabled by default.
+ */
+typedef enum psc_kernel {
+  PSC_K_PACK = 0,
+  PSC_K_ATTN_SCHEDULE = 1,
+  PSC_K_ATTN_FWD = 2,
+  PSC_K_ATTN_BWD_PRE = 3,
+  PSC_K_ATTN_BWD_DKDV = 4,
+  PSC_K_ATTN_BWD_DQ = 5
+} psc_kernel;
+
+int psc_timing_enable(int enable);
+int psc_timing_reset(void);
+int psc_timing_read(int kernel, double* total_ms /* host out */, int64_t* launches /* host out */);
+const char* psc_kernel_name(int kernel);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PSC_H_ */

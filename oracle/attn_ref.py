@@ -131,28 +131,32 @@ def attn_bwd(q, k, v, do, cu_seqlens, softmax_scale=None, block=512):
     return dq, dk, dv
 
 
+def _slice64(x, *idx):
+    """fp64 copy of x[idx] only (inputs at full size may be large bf16 arrays)."""
+    return _f64(x[idx])
+
+
 def attn_rows(q, k, v, cu_seqlens, rows, heads, softmax_scale=None):
-    """Forward outputs and dq for selected (token, head) pairs only, each from
+    """Forward output and lse for selected (token, head) pairs only, each from
     its own segment prefix; cheap spot checks at full size.
 
-    Returns o [n, D], lse [n]; when ``do`` style checks are needed use
-    ``attn_rows_bwd``.
+    Returns o [n, D], lse [n].
     """
-    q, k, v = _f64(q), _f64(k), _f64(v)
     D = q.shape[2]
     G = q.shape[1] // k.shape[1]
     scale = _scale(D, softmax_scale)
     cu = np.asarray(cu_seqlens).reshape(-1).astype(np.int64)
     outs, lses = [], []
     for t, h in zip(rows, heads):
+        t, h = int(t), int(h)
         sidx = int(np.searchsorted(cu, t, side="right")) - 1
         s = int(cu[sidx])
         g = h // G
-        srow = scale * (k[s:t + 1, g] @ q[t, h])
+        srow = scale * (_slice64(k, slice(s, t + 1), g) @ _slice64(q, t, h))
         m = srow.max()
         l = m + math.log(np.exp(srow - m).sum())
         p = np.exp(srow - l)
-        outs.append(p @ v[s:t + 1, g])
+        outs.append(p @ _slice64(v, slice(s, t + 1), g))
         lses.append(l)
     return np.array(outs), np.array(lses)
 
@@ -160,21 +164,56 @@ def attn_rows(q, k, v, cu_seqlens, rows, heads, softmax_scale=None):
 def attn_rows_dq(q, k, v, do, cu_seqlens, rows, heads, softmax_scale=None):
     """dq for selected (token, head) pairs; row t of dq depends only on row t's
     scores, so each is computed alone."""
-    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
     D = q.shape[2]
     G = q.shape[1] // k.shape[1]
     scale = _scale(D, softmax_scale)
     cu = np.asarray(cu_seqlens).reshape(-1).astype(np.int64)
     out = []
     for t, h in zip(rows, heads):
+        t, h = int(t), int(h)
         sidx = int(np.searchsorted(cu, t, side="right")) - 1
         s = int(cu[sidx])
         g = h // G
-        K, V = k[s:t + 1, g], v[s:t + 1, g]
-        srow = scale * (K @ q[t, h])
+        K, V = _slice64(k, slice(s, t + 1), g), _slice64(v, slice(s, t + 1), g)
+        srow = scale * (K @ _slice64(q, t, h))
         p = np.exp(srow - srow.max())
         p /= p.sum()
-        dp = V @ do[t, h]
+        dp = V @ _slice64(do, t, h)
         ds = p * (dp - (p * dp).sum())
         out.append(scale * (ds @ K))
     return np.array(out)
+
+
+def attn_bwd_keys(q, k, v, do, cu_seqlens, seg, key_lo, kv_heads, softmax_scale=None, block=512):
+    """dk, dv for the keys [key_lo, e) of segment ``seg`` = [s, e) and the
+    listed key/value heads only.
+
+    dk_j and dv_j need every query row i >= j of the document; each such row's
+    lse_i and D_i come from its full causal prefix, so rows [key_lo, e) are
+    computed in full and only the key columns >= key_lo are accumulated.
+    Returns arrays [e - key_lo, len(kv_heads), D].
+    """
+    Hq, D = q.shape[1], q.shape[2]
+    G = Hq // k.shape[1]
+    scale = _scale(D, softmax_scale)
+    cu = [int(c) for c in np.asarray(cu_seqlens).reshape(-1)]
+    s, e = cu[seg], cu[seg + 1]
+    n = e - key_lo
+    dk = np.zeros((n, len(kv_heads), D))
+    dv = np.zeros((n, len(kv_heads), D))
+    for gi, g in enumerate(kv_heads):
+        K, V = _slice64(k, slice(s, e), g), _slice64(v, slice(s, e), g)
+        for h in range(g * G, (g + 1) * G):
+            Q, dO = _slice64(q, slice(s, e), h), _slice64(do, slice(s, e), h)
+            for i0 in range(key_lo - s, e - s, block):
+                i1 = min(i0 + block, e - s)
+                S = _causal_block_scores(Q[i0:i1], K[:i1], i0, scale)
+                m = S.max(axis=1, keepdims=True)
+                P = np.exp(S - m)
+                P /= P.sum(axis=1, keepdims=True)
+                dP = dO[i0:i1] @ V[:i1].T
+                dS = P * (dP - (P * dP).sum(axis=1, keepdims=True))
+                c0 = key_lo - s
+                dk[: i1 - c0, gi] += scale * (dS[:, c0:].T @ Q[i0:i1])
+                dv[: i1 - c0, gi] += P[:, c0:].T @ dO[i0:i1]
+    return dk, dv

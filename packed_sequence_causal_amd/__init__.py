@@ -1,0 +1,253 @@
+"""Sample packing and document-causal attention on MI355X (gfx950).
+
+Thin ctypes binding over ``libpsc.so`` (C ABI in ``include/psc.h``).  It only
+marshals arguments: torch tensors provide device memory and the current HIP
+stream; every step of the computation runs in the library's HIP kernels.
+There is no fallback: without the built library every call raises.
+
+Entry points (same names as the C ABI without the ``psc_`` prefix):
+  pack_sizes, pack_build                  build_pack / build_unpack on the GPU
+  varlen_attn_workspace, varlen_attn_fwd, varlen_attn_bwd
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+PACK, UNPACK = 0, 1
+F32, BF16 = 0, 1
+
+OK = 0
+ERR_INVALID = -1
+ERR_UNSUPPORTED = -2
+ERR_WORKSPACE = -3
+ERR_CAPACITY = -4
+ERR_HIP = -5
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpsc.so")
+_lib = None
+
+_c_i64p = ctypes.POINTER(ctypes.c_int64)
+_c_sizep = ctypes.POINTER(ctypes.c_size_t)
+_vp = ctypes.c_void_p
+
+_SIGNATURES = {
+    "psc_strerror": (ctypes.c_char_p, [ctypes.c_int]),
+    "psc_version": (ctypes.c_int, []),
+    "psc_pack_sizes": (ctypes.c_int, [ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32,
+                                      ctypes.c_int32, _c_i64p, _c_i64p, _c_sizep]),
+    "psc_pack_build": (ctypes.c_int, [ctypes.c_int, _vp, _vp, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32,
+                                      ctypes.c_int32, ctypes.c_int64, _vp, _vp, _vp, _vp, ctypes.c_int64, _vp,
+                                      _vp, _vp, _vp, ctypes.c_size_t, _vp]),
+    "psc_timing_enable": (ctypes.c_int, [ctypes.c_int]),
+    "psc_timing_reset": (ctypes.c_int, []),
+    "psc_timing_read": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(ctypes.c_double), _c_i64p]),
+    "psc_kernel_name": (ctypes.c_char_p, [ctypes.c_int]),
+    "psc_varlen_attn_workspace": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, ctypes.c_int64, ctypes.c_int32,
+                                                 ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                                 _c_sizep]),
+    "psc_varlen_attn_fwd": (ctypes.c_int, [ctypes.c_int, _vp, _vp, _vp, ctypes.c_int64, ctypes.c_int64,
+                                           ctypes.c_int64, _vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
+                                           ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_float, _vp,
+                                           ctypes.c_int64, _vp, _vp, ctypes.c_size_t, _vp]),
+    "psc_varlen_attn_bwd": (ctypes.c_int, [ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int64,
+                                           ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, _vp,
+                                           ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32,
+                                           ctypes.c_int32, ctypes.c_int32, ctypes.c_float, _vp, _vp, _vp, _vp,
+                                           ctypes.c_size_t, _vp]),
+}
+
+
+class PscError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {strerror(status)} ({status})")
+
+
+def lib() -> ctypes.CDLL:
+    """Load libpsc.so (raises if it was not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing; build it with __graft_entry__.build() "
+                               "or python -m packed_sequence_causal_amd.build")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def strerror(status: int) -> str:
+    return lib().psc_strerror(status).decode()
+
+
+def _check(status: int, where: str):
+    if status != OK:
+        raise PscError(status, where)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+# ------------------------------------------------------------------ packing
+
+def pack_sizes(mode: int, n_docs: int, n_tokens: int, micro_bsz: int, seq_len: int):
+    """(n_rows, max_segments, workspace_bytes) for pack_build."""
+    rows, segs, ws = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_size_t()
+    _check(lib().psc_pack_sizes(mode, n_docs, n_tokens, micro_bsz, seq_len, ctypes.byref(rows),
+                                ctypes.byref(segs), ctypes.byref(ws)), "psc_pack_sizes")
+    return rows.value, segs.value, ws.value
+
+
+def pack_build(tokens, doc_offsets, micro_bsz: int, seq_len: int, mode: int = PACK, out: Optional[dict] = None,
+               workspace=None, stream=None) -> dict:
+    """Pack documents on the GPU.
+
+    tokens: int32 [n_tokens] device tensor; doc_offsets: int64 [n_docs + 1].
+    Returns device tensors input_ids, labels, indexes [n_rows, PL],
+    cu_seqlens [max_segments + 1] (valid up to stats[0]), row_seg_ptr
+    [n_rows + 1], row_valid_len [n_rows], stats [4] (n_seg, max_seqlen,
+    rows_filled, 0).  Pass ``out`` (a previous result) and ``workspace`` to
+    reuse buffers.
+    """
+    import torch
+
+    n_docs = doc_offsets.numel() - 1
+    n_tokens = tokens.numel()
+    rows, segs, ws = pack_sizes(mode, n_docs, n_tokens, micro_bsz, seq_len)
+    dev = tokens.device
+    PL = micro_bsz * seq_len
+    if out is None:
+        i32 = dict(dtype=torch.int32, device=dev)
+        out = {
+            "input_ids": torch.empty(rows, PL, **i32),
+            "labels": torch.empty(rows, PL, **i32),
+            "indexes": torch.empty(rows, PL, **i32),
+            "cu_seqlens": torch.empty(segs + 1, **i32),
+            "row_seg_ptr": torch.empty(rows + 1, **i32),
+            "row_valid_len": torch.empty(max(rows, 1), **i32),
+            "stats": torch.empty(4, **i32),
+        }
+    if workspace is None:
+        workspace = torch.empty(max(ws, 256), dtype=torch.uint8, device=dev)
+    _check(lib().psc_pack_build(mode, _ptr(tokens), _ptr(doc_offsets), n_docs, n_tokens, micro_bsz, seq_len,
+                                rows, _ptr(out["input_ids"]), _ptr(out["labels"]), _ptr(out["indexes"]),
+                                _ptr(out["cu_seqlens"]), out["cu_seqlens"].numel() - 1,
+                                _ptr(out["row_seg_ptr"]), _ptr(out["row_valid_len"]), _ptr(out["stats"]),
+                                _ptr(workspace), workspace.numel(), _stream(stream)), "psc_pack_build")
+    out["_workspace"] = workspace
+    return out
+
+
+# ---------------------------------------------------------------- attention
+
+def _dtype_code(t):
+    import torch
+
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _tok_stride(t, name):
+    if t.dim() != 3 or t.stride(2) != 1 or t.stride(1) != t.shape[2]:
+        raise ValueError(f"{name} must be [T, heads, D] with unit dim stride and head stride D")
+    return t.stride(0)
+
+
+def varlen_attn_workspace(pass_: int, dtype: int, total_tokens: int, n_segments: int, max_seqlen: int,
+                          hq: int, hkv: int, head_dim: int) -> int:
+    b = ctypes.c_size_t()
+    _check(lib().psc_varlen_attn_workspace(pass_, dtype, total_tokens, n_segments, max_seqlen, hq, hkv, head_dim,
+                                           ctypes.byref(b)), "psc_varlen_attn_workspace")
+    return b.value
+
+
+def varlen_attn_fwd(q, k, v, cu_seqlens, max_seqlen: int, n_segments: Optional[int] = None,
+                    softmax_scale: Optional[float] = None, out=None, lse=None, workspace=None, stream=None):
+    """Forward pass.  q [T,hq,D], k/v [T,hkv,D] (views allowed), cu_seqlens
+    int32 [n_segments + 1].  Returns (out [T,hq,D], lse float32 [hq,T])."""
+    import torch
+
+    T, hq, D = q.shape
+    hkv = k.shape[1]
+    dt = _dtype_code(q)
+    nseg = cu_seqlens.numel() - 1 if n_segments is None else n_segments
+    if out is None:
+        out = torch.empty(T, hq, D, dtype=q.dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty(hq, T, dtype=torch.float32, device=q.device)
+    ws = varlen_attn_workspace(0, dt, T, nseg, max_seqlen, hq, hkv, D)
+    if workspace is None or workspace.numel() < ws:
+        workspace = torch.empty(max(ws, 256), dtype=torch.uint8, device=q.device)
+    _check(lib().psc_varlen_attn_fwd(dt, _ptr(q), _ptr(k), _ptr(v), _tok_stride(q, "q"), _tok_stride(k, "k"),
+                                     _tok_stride(v, "v"), _ptr(cu_seqlens), nseg, max_seqlen, T, hq, hkv, D,
+                                     float(softmax_scale or 0.0), _ptr(out), _tok_stride(out, "out"), _ptr(lse),
+                                     _ptr(workspace), workspace.numel(), _stream(stream)), "psc_varlen_attn_fwd")
+    return out, lse
+
+
+def varlen_attn_bwd(q, k, v, out, dout, lse, cu_seqlens, max_seqlen: int, n_segments: Optional[int] = None,
+                    softmax_scale: Optional[float] = None, dq=None, dk=None, dv=None, workspace=None,
+                    stream=None):
+    """Backward pass.  Returns fp32 (dq [T,hq,D], dk [T,hkv,D], dv [T,hkv,D])."""
+    import torch
+
+    T, hq, D = q.shape
+    hkv = k.shape[1]
+    dt = _dtype_code(q)
+    nseg = cu_seqlens.numel() - 1 if n_segments is None else n_segments
+    f32 = dict(dtype=torch.float32, device=q.device)
+    dq = torch.empty(T, hq, D, **f32) if dq is None else dq
+    dk = torch.empty(T, hkv, D, **f32) if dk is None else dk
+    dv = torch.empty(T, hkv, D, **f32) if dv is None else dv
+    ws = varlen_attn_workspace(1, dt, T, nseg, max_seqlen, hq, hkv, D)
+    if workspace is None or workspace.numel() < ws:
+        workspace = torch.empty(max(ws, 256), dtype=torch.uint8, device=q.device)
+    _check(lib().psc_varlen_attn_bwd(dt, _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse),
+                                     _tok_stride(q, "q"), _tok_stride(k, "k"), _tok_stride(v, "v"),
+                                     _tok_stride(out, "out"), _tok_stride(dout, "dout"), _ptr(cu_seqlens), nseg,
+                                     max_seqlen, T, hq, hkv, D, float(softmax_scale or 0.0), _ptr(dq), _ptr(dk),
+                                     _ptr(dv), _ptr(workspace), workspace.numel(), _stream(stream)),
+           "psc_varlen_attn_bwd")
+    return dq, dk, dv
+
+
+# ---------------------------------------------------------- instrumentation
+
+KERNELS = {"pack": 0, "attn_schedule": 1, "attn_fwd": 2, "attn_bwd_pre": 3, "attn_bwd_dkdv": 4, "attn_bwd_dq": 5}
+
+
+def timing_enable(on: bool = True):
+    _check(lib().psc_timing_enable(1 if on else 0), "psc_timing_enable")
+
+
+def timing_reset():
+    _check(lib().psc_timing_reset(), "psc_timing_reset")
+
+
+def timing_read() -> dict:
+    """{kernel name: (total_ms, launches)} since the last reset; waits for the
+    recorded events."""
+    out = {}
+    for name, kid in KERNELS.items():
+        ms, n = ctypes.c_double(), ctypes.c_int64()
+        _check(lib().psc_timing_read(kid, ctypes.byref(ms), ctypes.byref(n)), "psc_timing_read")
+        out[name] = (ms.value, n.value)
+    return out

@@ -1,0 +1,134 @@
+// Tile schedule built from cu_seqlens on the GPU.
+//
+// Every segment [c_s, c_{s+1}) is cut into tiles of `tile` rows counted from
+// the segment's own start, so no tile straddles two documents.  A tile's work
+// is the length of the key (or query) range it must visit:
+//   prefix mode (forward, dQ): query tile t visits keys [0, min((t+1)*tile, L))
+//   suffix mode (dK/dV):       key tile t visits queries [t*tile, L)
+// Tiles outside a document's causal triangle are never listed ("Sample
+// Packing：长序列 LLM 训练的 Attention 问题及优化", section 5.1: all-zero mask
+// tiles need no work; the varlen decomposition turns the block-diagonal mask
+// into one causal problem per document).
+//
+// Tiles are ordered by decreasing work (longest processing time first) with a
+// counting sort over work measured in `unit`-row blocks: histogram, descending
+// exclusive scan, scatter.  Ties are placed in atomic order; each tile's result
+// does not depend on the order.
+#include "psc_internal.h"
+
+namespace psc {
+namespace {
+
+constexpr int kThreads = 256;
+
+__device__ inline int32_t tile_work(int32_t L, int32_t t, int32_t tile, bool suffix) {
+  return suffix ? L - t * tile : min((t + 1) * tile, L);
+}
+
+__global__ void k_sched_zero(int32_t* hist, int32_t n_bins, int32_t* n_items) {
+  for (int32_t i = blockIdx.x * kThreads + threadIdx.x; i < n_bins; i += gridDim.x * kThreads) hist[i] = 0;
+  if (blockIdx.x == 0 && threadIdx.x == 0) *n_items = 0;
+}
+
+__device__ inline int32_t seg_len(const int32_t* cu, int32_t s, int32_t T) {
+  const int32_t a = min(max(cu[s], 0), T);
+  return min(max(cu[s + 1], a), T) - a;
+}
+
+__global__ void k_sched_count(const int32_t* cu, int32_t n_seg, int32_t T, int32_t tile, int32_t unit, bool suffix,
+                              int32_t* hist, int32_t n_bins) {
+  const int32_t s = blockIdx.x * kThreads + threadIdx.x;
+  if (s >= n_seg) return;
+  const int32_t L = seg_len(cu, s, T);
+  if (L <= 0) return;
+  const int32_t nt = (L + tile - 1) / tile;
+  for (int32_t t = 0; t < nt; ++t) {
+    const int32_t bin = min((tile_work(L, t, tile, suffix) + unit - 1) / unit, n_bins - 1);
+    atomicAdd(&hist[bin], 1);
+  }
+}
+
+// Descending exclusive scan: cursor[b] = number of tiles in bins > b.
+__global__ void k_sched_scan(int32_t* hist, int32_t n_bins, int32_t* n_items) {
+  __shared__ int32_t wsum[kThreads / 64];
+  int32_t carry = 0;
+  for (int32_t c = 0; c < n_bins; c += kThreads) {
+    const int32_t i = c + threadIdx.x;
+    const int32_t b = n_bins - 1 - i;  // walk bins from the top
+    int32_t v = i < n_bins ? hist[b] : 0;
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    int32_t x = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      int32_t y = __shfl_up(x, o, 64);
+      if (lane >= o) x += y;
+    }
+    if (lane == 63) wsum[wid] = x;
+    __syncthreads();
+    int32_t off = 0, tot = 0;
+    for (int w = 0; w < kThreads / 64; ++w) {
+      if (w < wid) off += wsum[w];
+      tot += wsum[w];
+    }
+    __syncthreads();
+    if (i < n_bins) hist[b] = carry + off + x - v;
+    carry += tot;
+  }
+  if (threadIdx.x == 0) *n_items = carry;
+}
+
+__global__ void k_sched_fill(const int32_t* cu, int32_t n_seg, int32_t T, int32_t tile, int32_t unit, bool suffix,
+                             int32_t* hist, int32_t n_bins, int32_t* items, int64_t cap) {
+  const int32_t s = blockIdx.x * kThreads + threadIdx.x;
+  if (s >= n_seg) return;
+  const int32_t L = seg_len(cu, s, T);
+  if (L <= 0) return;
+  const int32_t nt = (L + tile - 1) / tile;
+  for (int32_t t = 0; t < nt; ++t) {
+    const int32_t bin = min((tile_work(L, t, tile, suffix) + unit - 1) / unit, n_bins - 1);
+    const int32_t pos = atomicAdd(&hist[bin], 1);
+    if (pos < cap) {
+      items[2 * pos] = s;
+      items[2 * pos + 1] = t;
+    }
+  }
+}
+
+}  // namespace
+
+// Upper bound on the number of tiles: sum over segments of ceil(L / tile)
+// <= T / tile + n_seg.
+static int64_t sched_cap(int64_t T, int32_t n_seg, int tile) { return T / tile + n_seg + 1; }
+static int32_t sched_bins(int32_t max_seqlen, int unit) { return (max_seqlen + unit - 1) / unit + 2; }
+
+size_t schedule_bytes(int64_t T, int32_t n_seg, int32_t max_seqlen, int tile, int unit) {
+  return align_up(sizeof(int32_t) * 2 * sched_cap(T, n_seg, tile), 256) +
+         align_up(sizeof(int32_t) * sched_bins(max_seqlen, unit), 256) + 256;
+}
+
+TileSchedule schedule_carve(void* ws, int64_t T, int32_t n_seg, int32_t max_seqlen, int tile, int unit) {
+  TileSchedule s;
+  char* p = static_cast<char*>(ws);
+  s.cap = sched_cap(T, n_seg, tile);
+  s.n_bins = sched_bins(max_seqlen, unit);
+  s.items = reinterpret_cast<int32_t*>(p);
+  p += align_up(sizeof(int32_t) * 2 * s.cap, 256);
+  s.hist = reinterpret_cast<int32_t*>(p);
+  p += align_up(sizeof(int32_t) * s.n_bins, 256);
+  s.n_items = reinterpret_cast<int32_t*>(p);
+  return s;
+}
+
+hipError_t launch_schedule(const int32_t* cu, int32_t n_seg, int32_t T, int tile, int unit, bool suffix,
+                           const TileSchedule& s, hipStream_t stream) {
+  ScopedKernelTimer timed(kTimeSchedule, stream);
+  const unsigned gs = (unsigned)((n_seg + kThreads - 1) / kThreads);
+  k_sched_zero<<<(s.n_bins + kThreads - 1) / kThreads, kThreads, 0, stream>>>(s.hist, s.n_bins, s.n_items);
+  if (n_seg > 0) k_sched_count<<<gs, kThreads, 0, stream>>>(cu, n_seg, T, tile, unit, suffix, s.hist, s.n_bins);
+  k_sched_scan<<<1, kThreads, 0, stream>>>(s.hist, s.n_bins, s.n_items);
+  if (n_seg > 0)
+    k_sched_fill<<<gs, kThreads, 0, stream>>>(cu, n_seg, T, tile, unit, suffix, s.hist, s.n_bins, s.items, s.cap);
+  return hipGetLastError();
+}
+
+}  // namespace psc

@@ -1,0 +1,234 @@
+// C ABI of libpsc.so (declared in include/psc.h): argument checks, sizing,
+// workspace carving and launches on the caller's stream.  Every check runs on
+// the host before anything is enqueued; no HIP call is made on an error path.
+#include <cmath>
+#include <cstdint>
+#include <limits>
+
+#include "../../include/psc.h"
+#include "psc_internal.h"
+
+namespace {
+
+constexpr int64_t kMaxPacked = int64_t(1) << 30;
+constexpr int64_t kI32Max = std::numeric_limits<int32_t>::max();
+
+int pack_dims(int mode, int64_t n_docs, int64_t n_tokens, int32_t micro_bsz, int32_t seq_len,
+              int64_t* n_rows, int64_t* max_segments) {
+  if (mode != PSC_BUILD_PACK && mode != PSC_BUILD_UNPACK) return PSC_ERR_INVALID;
+  if (n_docs < 0 || n_tokens < 0 || micro_bsz < 1 || seq_len < 1) return PSC_ERR_INVALID;
+  const int64_t PL = (int64_t)micro_bsz * seq_len;
+  if (PL > kMaxPacked) return PSC_ERR_INVALID;
+  if (n_docs >= kI32Max || n_tokens >= kI32Max) return PSC_ERR_INVALID;
+  const int64_t rows = mode == PSC_BUILD_PACK ? (n_tokens + PL - 1) / PL : (n_docs + micro_bsz - 1) / micro_bsz;
+  if (rows * PL > kI32Max) return PSC_ERR_INVALID;  // cu_seqlens is int32
+  const int64_t segs = mode == PSC_BUILD_PACK ? n_docs + 2 * rows : n_docs + rows;
+  if (segs >= kI32Max) return PSC_ERR_INVALID;
+  *n_rows = rows;
+  *max_segments = segs;
+  return PSC_OK;
+}
+
+bool supported_head_dim(int dtype, int32_t d) {
+  if (dtype == PSC_BF16) return d == 64 || d == 128;
+  return d == 32 || d == 64 || d == 128;
+}
+
+int attn_dims(int dtype, int64_t T, int32_t n_seg, int32_t max_seqlen, int32_t hq, int32_t hkv, int32_t head_dim,
+              float softmax_scale, psc::AttnDims* out) {
+  if (dtype != PSC_F32 && dtype != PSC_BF16) return PSC_ERR_INVALID;
+  if (T < 0 || T > kI32Max || n_seg < 0 || hq < 1 || hkv < 1 || head_dim < 1) return PSC_ERR_INVALID;
+  if (hq % hkv != 0) return PSC_ERR_INVALID;
+  if (T > 0 && (n_seg < 1 || n_seg > T || max_seqlen < 1 || max_seqlen > T)) return PSC_ERR_INVALID;
+  if (!supported_head_dim(dtype, head_dim)) return PSC_ERR_UNSUPPORTED;
+  if (!(softmax_scale == softmax_scale) || std::isinf(softmax_scale)) return PSC_ERR_INVALID;
+  out->T = T;
+  out->n_seg = n_seg;
+  out->max_seqlen = max_seqlen < 1 ? 1 : max_seqlen;
+  out->hq = hq;
+  out->hkv = hkv;
+  out->d = head_dim;
+  out->scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)head_dim);
+  return PSC_OK;
+}
+
+// Token stride and base alignment of one [T, heads, D] operand.
+bool operand_ok(const void* p, int64_t tok_stride, int32_t heads, int32_t d, int dtype, int64_t T) {
+  if (T == 0) return true;
+  if (!p) return false;
+  if (tok_stride < (int64_t)heads * d) return false;
+  if (dtype == PSC_BF16) {
+    if (reinterpret_cast<uintptr_t>(p) % 16 != 0) return false;
+    if ((tok_stride * 2) % 16 != 0) return false;
+  } else {
+    if (reinterpret_cast<uintptr_t>(p) % 4 != 0) return false;
+  }
+  return true;
+}
+
+size_t workspace_for(int pass, int dtype, const psc::AttnDims& d) {
+  return pass == 0 ? psc::attn_fwd_workspace_bytes(dtype, d) : psc::attn_bwd_workspace_bytes(dtype, d);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* psc_strerror(int status) {
+  switch (status) {
+    case PSC_OK: return "ok";
+    case PSC_ERR_INVALID: return "invalid argument";
+    case PSC_ERR_UNSUPPORTED: return "unsupported configuration";
+    case PSC_ERR_WORKSPACE: return "workspace missing or too small";
+    case PSC_ERR_CAPACITY: return "output capacity too small";
+    case PSC_ERR_HIP: return "HIP runtime error at launch";
+    default: return "unknown status";
+  }
+}
+
+int psc_version(void) { return 100; }
+
+int psc_pack_sizes(int mode, int64_t n_docs, int64_t n_tokens, int32_t micro_bsz, int32_t seq_len,
+                   int64_t* n_rows, int64_t* max_segments, size_t* workspace_bytes) {
+  if (!n_rows || !max_segments || !workspace_bytes) return PSC_ERR_INVALID;
+  int64_t rows, segs;
+  int st = pack_dims(mode, n_docs, n_tokens, micro_bsz, seq_len, &rows, &segs);
+  if (st != PSC_OK) return st;
+  *n_rows = rows;
+  *max_segments = segs;
+  *workspace_bytes = psc::pack_workspace_bytes(n_docs, rows);
+  return PSC_OK;
+}
+
+int psc_pack_build(int mode, const int32_t* tokens, const int64_t* doc_offsets, int64_t n_docs, int64_t n_tokens,
+                   int32_t micro_bsz, int32_t seq_len, int64_t n_rows, int32_t* input_ids, int32_t* labels,
+                   int32_t* indexes, int32_t* cu_seqlens, int64_t max_segments, int32_t* row_seg_ptr,
+                   int32_t* row_valid_len, int32_t* stats, void* workspace, size_t workspace_bytes,
+                   void* stream) {
+  int64_t rows, segs;
+  int st = pack_dims(mode, n_docs, n_tokens, micro_bsz, seq_len, &rows, &segs);
+  if (st != PSC_OK) return st;
+  if (n_rows != rows) return PSC_ERR_INVALID;
+  if (!doc_offsets || !cu_seqlens || !row_seg_ptr || !stats) return PSC_ERR_INVALID;
+  if (n_tokens > 0 && !tokens) return PSC_ERR_INVALID;
+  if (rows > 0 && (!input_ids || !labels || !indexes)) return PSC_ERR_INVALID;
+  if (n_docs == 0 && n_tokens != 0) return PSC_ERR_INVALID;
+  if (max_segments < segs) return PSC_ERR_CAPACITY;
+  const size_t need = psc::pack_workspace_bytes(n_docs, rows);
+  if (!workspace || workspace_bytes < need) return PSC_ERR_WORKSPACE;
+
+  psc::PackArgs a;
+  a.mode = mode;
+  a.tokens = tokens;
+  a.doc_offsets = doc_offsets;
+  a.n_docs = n_docs;
+  a.n_tokens = n_tokens;
+  a.micro_bsz = micro_bsz;
+  a.seq_len = seq_len;
+  a.packed_length = micro_bsz * seq_len;
+  a.n_rows = rows;
+  a.input_ids = input_ids;
+  a.labels = labels;
+  a.indexes = indexes;
+  a.cu_seqlens = cu_seqlens;
+  a.row_seg_ptr = row_seg_ptr;
+  a.row_valid_len = row_valid_len;
+  a.stats = stats;
+  a.max_segments = max_segments;
+  a.workspace = workspace;
+  return psc::launch_pack(a, static_cast<hipStream_t>(stream)) == hipSuccess ? PSC_OK : PSC_ERR_HIP;
+}
+
+int psc_varlen_attn_workspace(int pass, int dtype, int64_t total_tokens, int32_t n_segments, int32_t max_seqlen,
+                              int32_t hq, int32_t hkv, int32_t head_dim, size_t* bytes) {
+  if (!bytes || (pass != 0 && pass != 1)) return PSC_ERR_INVALID;
+  psc::AttnDims d;
+  int st = attn_dims(dtype, total_tokens, n_segments, max_seqlen, hq, hkv, head_dim, 0.f, &d);
+  if (st != PSC_OK) return st;
+  *bytes = workspace_for(pass, dtype, d);
+  return PSC_OK;
+}
+
+int psc_varlen_attn_fwd(int dtype, const void* q, const void* k, const void* v, int64_t q_tok_stride,
+                        int64_t k_tok_stride, int64_t v_tok_stride, const int32_t* cu_seqlens, int32_t n_segments,
+                        int32_t max_seqlen, int64_t total_tokens, int32_t hq, int32_t hkv, int32_t head_dim,
+                        float softmax_scale, void* out, int64_t out_tok_stride, float* lse, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  psc::AttnDims d;
+  int st = attn_dims(dtype, total_tokens, n_segments, max_seqlen, hq, hkv, head_dim, softmax_scale, &d);
+  if (st != PSC_OK) return st;
+  const int64_t T = total_tokens;
+  if (!operand_ok(q, q_tok_stride, hq, head_dim, dtype, T) || !operand_ok(k, k_tok_stride, hkv, head_dim, dtype, T) ||
+      !operand_ok(v, v_tok_stride, hkv, head_dim, dtype, T) ||
+      !operand_ok(out, out_tok_stride, hq, head_dim, dtype, T))
+    return PSC_ERR_INVALID;
+  if (T > 0 && (!cu_seqlens || !lse)) return PSC_ERR_INVALID;
+  const size_t need = workspace_for(0, dtype, d);
+  if (T > 0 && (!workspace || workspace_bytes < need)) return PSC_ERR_WORKSPACE;
+  if (T == 0) return PSC_OK;
+
+  psc::AttnFwdArgs a;
+  a.dims = d;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.sq = q_tok_stride;
+  a.sk = k_tok_stride;
+  a.sv = v_tok_stride;
+  a.so = out_tok_stride;
+  a.cu = cu_seqlens;
+  a.out = out;
+  a.lse = lse;
+  a.workspace = workspace;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = dtype == PSC_BF16 ? psc::launch_attn_fwd_bf16(a, s) : psc::launch_attn_fwd_f32(a, s);
+  return e == hipSuccess ? PSC_OK : PSC_ERR_HIP;
+}
+
+int psc_varlen_attn_bwd(int dtype, const void* q, const void* k, const void* v, const void* out, const void* dout,
+                        const float* lse, int64_t q_tok_stride, int64_t k_tok_stride, int64_t v_tok_stride,
+                        int64_t out_tok_stride, int64_t dout_tok_stride, const int32_t* cu_seqlens,
+                        int32_t n_segments, int32_t max_seqlen, int64_t total_tokens, int32_t hq, int32_t hkv,
+                        int32_t head_dim, float softmax_scale, float* dq, float* dk, float* dv, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  psc::AttnDims d;
+  int st = attn_dims(dtype, total_tokens, n_segments, max_seqlen, hq, hkv, head_dim, softmax_scale, &d);
+  if (st != PSC_OK) return st;
+  const int64_t T = total_tokens;
+  if (!operand_ok(q, q_tok_stride, hq, head_dim, dtype, T) || !operand_ok(k, k_tok_stride, hkv, head_dim, dtype, T) ||
+      !operand_ok(v, v_tok_stride, hkv, head_dim, dtype, T) ||
+      !operand_ok(out, out_tok_stride, hq, head_dim, dtype, T) ||
+      !operand_ok(dout, dout_tok_stride, hq, head_dim, dtype, T))
+    return PSC_ERR_INVALID;
+  if (T > 0 && (!cu_seqlens || !lse || !dq || !dk || !dv)) return PSC_ERR_INVALID;
+  if (T > 0 && ((reinterpret_cast<uintptr_t>(dq) | reinterpret_cast<uintptr_t>(dk) |
+                 reinterpret_cast<uintptr_t>(dv)) % 16 != 0))
+    return PSC_ERR_INVALID;
+  const size_t need = workspace_for(1, dtype, d);
+  if (T > 0 && (!workspace || workspace_bytes < need)) return PSC_ERR_WORKSPACE;
+  if (T == 0) return PSC_OK;
+
+  psc::AttnBwdArgs a;
+  a.dims = d;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = out;
+  a.dout = dout;
+  a.lse = lse;
+  a.sq = q_tok_stride;
+  a.sk = k_tok_stride;
+  a.sv = v_tok_stride;
+  a.so = out_tok_stride;
+  a.sdo = dout_tok_stride;
+  a.cu = cu_seqlens;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.workspace = workspace;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = dtype == PSC_BF16 ? psc::launch_attn_bwd_bf16(a, s) : psc::launch_attn_bwd_f32(a, s);
+  return e == hipSuccess ? PSC_OK : PSC_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,147 @@
+"""C ABI checks that need no GPU: the library loads, exports every function
+include/psc.h declares, sizes come out as documented, and invalid arguments
+are rejected on the host (these paths make no HIP call)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import packed_sequence_causal_amd as psc
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "psc.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(psc.LIB_PATH), reason="libpsc.so not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(psc_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert {"psc_pack_build", "psc_varlen_attn_fwd", "psc_varlen_attn_bwd"} <= set(names)
+    L = psc.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(psc._SIGNATURES), "binding and header disagree"
+
+
+def test_strerror_and_version():
+    assert psc.strerror(0) == "ok"
+    assert "workspace" in psc.strerror(psc.ERR_WORKSPACE)
+    assert psc.lib().psc_version() >= 100
+
+
+@pytest.mark.parametrize("mode,n_docs,n_tok,mb,sl,rows,segs", [
+    (psc.PACK, 4, 24, 2, 8, 2, 8),
+    (psc.UNPACK, 6, 44, 2, 8, 3, 9),
+    (psc.PACK, 0, 0, 2, 8, 0, 0),
+    (psc.PACK, 47, 70000, 1, 32768, 3, 53),
+    (psc.UNPACK, 980, 100000, 16, 2048, 62, 1042),
+])
+def test_pack_sizes(mode, n_docs, n_tok, mb, sl, rows, segs):
+    r, s, ws = psc.pack_sizes(mode, n_docs, n_tok, mb, sl)
+    assert (r, s) == (rows, segs)
+    assert ws > 0
+
+
+@pytest.mark.parametrize("args", [
+    (2, 4, 24, 2, 8),          # unknown mode
+    (0, -1, 24, 2, 8),         # negative docs
+    (0, 4, 24, 0, 8),          # micro_bsz < 1
+    (0, 4, 24, 2, 0),          # seq_len < 1
+    (0, 4, 24, 1 << 16, 1 << 15),  # packed length beyond 2^30
+])
+def test_pack_sizes_rejects(args):
+    with pytest.raises(psc.PscError) as e:
+        psc.pack_sizes(*args)
+    assert e.value.status == psc.ERR_INVALID
+
+
+def _pack_build_raw(**kw):
+    a = dict(mode=0, tokens=1, offs=1, n_docs=4, n_tok=24, mb=2, sl=8, rows=2, ids=1, lab=1, idx=1, cu=1, cap=8,
+             rsp=1, rvl=None, stats=1, ws=1, wsb=1 << 20)
+    a.update(kw)
+    v = lambda x: None if x is None else ctypes.c_void_p(x)
+    return psc.lib().psc_pack_build(a["mode"], v(a["tokens"]), v(a["offs"]), a["n_docs"], a["n_tok"], a["mb"],
+                                    a["sl"], a["rows"], v(a["ids"]), v(a["lab"]), v(a["idx"]), v(a["cu"]),
+                                    a["cap"], v(a["rsp"]), v(a["rvl"]), v(a["stats"]), v(a["ws"]), a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(rows=3), psc.ERR_INVALID),
+    (dict(offs=None), psc.ERR_INVALID),
+    (dict(tokens=None), psc.ERR_INVALID),
+    (dict(ids=None), psc.ERR_INVALID),
+    (dict(stats=None), psc.ERR_INVALID),
+    (dict(cap=7), psc.ERR_CAPACITY),
+    (dict(ws=None), psc.ERR_WORKSPACE),
+    (dict(wsb=16), psc.ERR_WORKSPACE),
+    (dict(n_docs=0, n_tok=24), psc.ERR_INVALID),
+])
+def test_pack_build_rejects_on_host(kw, code):
+    assert _pack_build_raw(**kw) == code
+
+
+def _fwd_raw(**kw):
+    a = dict(dtype=psc.BF16, q=16, k=16, v=16, sq=256, sk=128, sv=128, cu=16, nseg=1, maxlen=16, T=16, hq=2, hkv=1,
+             d=128, scale=0.0, out=16, so=256, lse=16, ws=16, wsb=1 << 24)
+    a.update(kw)
+    v = lambda x: None if x is None else ctypes.c_void_p(x)
+    return psc.lib().psc_varlen_attn_fwd(a["dtype"], v(a["q"]), v(a["k"]), v(a["v"]), a["sq"], a["sk"], a["sv"],
+                                         v(a["cu"]), a["nseg"], a["maxlen"], a["T"], a["hq"], a["hkv"], a["d"],
+                                         a["scale"], v(a["out"]), a["so"], v(a["lse"]), v(a["ws"]), a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(d=96), psc.ERR_UNSUPPORTED),
+    (dict(d=32), psc.ERR_UNSUPPORTED),          # bf16 needs 64 or 128
+    (dict(hq=3, hkv=2), psc.ERR_INVALID),        # hq % hkv != 0
+    (dict(dtype=7), psc.ERR_INVALID),
+    (dict(q=None), psc.ERR_INVALID),
+    (dict(q=8), psc.ERR_INVALID),                # misaligned base for bf16
+    (dict(sq=200), psc.ERR_INVALID),             # stride below heads*D
+    (dict(sk=130), psc.ERR_INVALID),             # stride*2 not a multiple of 16 bytes
+    (dict(cu=None), psc.ERR_INVALID),
+    (dict(lse=None), psc.ERR_INVALID),
+    (dict(nseg=0), psc.ERR_INVALID),
+    (dict(maxlen=17), psc.ERR_INVALID),          # longer than T
+    (dict(ws=None), psc.ERR_WORKSPACE),
+    (dict(wsb=8), psc.ERR_WORKSPACE),
+    (dict(scale=float("nan")), psc.ERR_INVALID),
+])
+def test_attn_fwd_rejects_on_host(kw, code):
+    assert _fwd_raw(**kw) == code
+
+
+def test_attn_empty_is_a_no_op():
+    assert _fwd_raw(T=0, nseg=0, maxlen=0, q=None, k=None, v=None, out=None, lse=None, cu=None, ws=None) == 0
+
+
+def test_attn_bwd_rejects_on_host():
+    v = lambda x: None if x is None else ctypes.c_void_p(x)
+    L = psc.lib()
+    base = [psc.BF16, v(16), v(16), v(16), v(16), v(16), v(16), 256, 128, 128, 256, 256, v(16), 1, 16, 16, 2, 1,
+            128, 0.0, v(16), v(16), v(16), v(16), 1 << 24, None]
+    bad_dq = list(base)
+    bad_dq[20] = None
+    assert L.psc_varlen_attn_bwd(*bad_dq) == psc.ERR_INVALID
+    bad_hd = list(base)
+    bad_hd[18] = 48
+    assert L.psc_varlen_attn_bwd(*bad_hd) == psc.ERR_UNSUPPORTED
+    mis = list(base)
+    mis[21] = v(20)  # dk not 16-byte aligned
+    assert L.psc_varlen_attn_bwd(*mis) == psc.ERR_INVALID
+
+
+def test_attn_workspace_sizes():
+    fwd = psc.varlen_attn_workspace(0, psc.BF16, 65536, 48, 4654, 32, 8, 128)
+    bwd = psc.varlen_attn_workspace(1, psc.BF16, 65536, 48, 4654, 32, 8, 128)
+    assert 0 < fwd < (1 << 20)
+    assert bwd >= 4 * 32 * 65536  # D row sums in fp32
+    with pytest.raises(psc.PscError):
+        psc.varlen_attn_workspace(2, psc.BF16, 16, 1, 16, 2, 1, 128)

@@ -1,0 +1,217 @@
+"""GPU document-causal attention vs the fp64 oracle.
+
+Tolerances: fp32 inputs max-abs 1e-5; bf16 inputs max-abs 2e-2 and rel-L2
+(||x - ref|| / ||ref|| over the compared elements) <= 5e-3, on O, lse, dQ, dK
+and dV.  Small cases compare every element against the full oracle; the
+full-size workloads, run exactly as the benchmark launches them, compare
+sampled outputs that the oracle computes one by one (random and tail rows of
+O / lse / dQ, the key tail of the longest document and whole short documents
+for dK / dV).  Also: results repeat bit for bit, writes stay inside their
+buffers (guard bands), and k / v may be strided views of one packed kv buffer.
+"""
+import numpy as np
+import pytest
+import torch
+
+import packed_sequence_causal_amd as psc
+from oracle import attn_ref, pack_ref
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+BF16_MAX_ABS, BF16_REL_L2 = 2e-2, 5e-3
+F32_MAX_ABS = 1e-5
+
+
+def close(name, got, ref, dtype):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, (name, got.shape, ref.shape)
+    assert np.isfinite(got).all(), name
+    err = np.abs(got - ref)
+    mx = float(err.max()) if err.size else 0.0
+    if dtype == "f32":
+        assert mx <= F32_MAX_ABS, f"{name}: max-abs {mx:.3e}"
+        return
+    rel = float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-30))
+    assert mx <= BF16_MAX_ABS and rel <= BF16_REL_L2, f"{name}: max-abs {mx:.3e} rel-L2 {rel:.3e}"
+
+
+def run(q, k, v, do, cu, backward=True, scale=None):
+    dev = torch.device("cuda:0")
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    cud = torch.as_tensor(np.asarray(cu, dtype=np.int32)).to(dev)
+    maxlen = int(np.diff(np.asarray(cu)).max())
+    out, lse = psc.varlen_attn_fwd(qd, kd, vd, cud, maxlen, softmax_scale=scale)
+    res = {"o": out, "lse": lse}
+    if backward:
+        dq, dk, dv = psc.varlen_attn_bwd(qd, kd, vd, out, do.to(dev), lse, cud, maxlen, softmax_scale=scale)
+        res.update(dq=dq, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    return {key: val.float().cpu() for key, val in res.items()}
+
+
+def full_compare(q, k, v, do, cu, dtype, backward=True, scale=None):
+    got = run(q, k, v, do, cu, backward, scale)
+    o, lse = attn_ref.attn_fwd(q, k, v, cu, softmax_scale=scale)
+    close("o", got["o"], o, dtype)
+    close("lse", got["lse"], lse, dtype)
+    if backward:
+        dq, dk, dv = attn_ref.attn_bwd(q, k, v, do, cu, softmax_scale=scale)
+        close("dq", got["dq"], dq, dtype)
+        close("dk", got["dk"], dk, dtype)
+        close("dv", got["dv"], dv, dtype)
+    return got
+
+
+# ------------------------------------------------------------- fp32 path
+
+def test_tiny_fp32_workload():
+    w = workloads.make("tiny")
+    cu = w.attn_cu_seqlens
+    q, k, v, do = workloads.qkv_do(16, 2, 2, 32, seed=0, dtype="f32")
+    full_compare(q, k, v, do, cu, "f32")
+
+
+@pytest.mark.parametrize("hq,hkv,D,seed", [(4, 2, 32, 1), (2, 1, 64, 2), (3, 3, 128, 3)])
+def test_fp32_random_layouts(hq, hkv, D, seed):
+    rng = np.random.default_rng(seed)
+    T = 240
+    cu = workloads.random_layout(rng, T, 1, 60)
+    q, k, v, do = workloads.qkv_do(T, hq, hkv, D, seed=seed, dtype="f32")
+    full_compare(q, k, v, do, cu, "f32")
+
+
+# ------------------------------------------------------------- bf16 path
+
+# segment lengths around the 64 / 128 tile edges, one-token documents, and a
+# longer document with a ragged tail
+EDGE_LAYOUT = [1, 63, 64, 65, 127, 128, 129, 1, 1, 200, 300, 431]
+
+
+@pytest.mark.parametrize("hq,hkv,D", [(8, 2, 128), (4, 4, 64), (4, 1, 128), (6, 3, 64)])
+def test_bf16_edge_layout(hq, hkv, D):
+    cu = np.concatenate([[0], np.cumsum(EDGE_LAYOUT)]).astype(np.int32)
+    T = int(cu[-1])
+    q, k, v, do = workloads.qkv_do(T, hq, hkv, D, seed=hq * 10 + D, dtype="bf16")
+    full_compare(q, k, v, do, cu, "bf16")
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_bf16_random_layouts(seed):
+    rng = np.random.default_rng(500 + seed)
+    T = int(rng.integers(900, 2500))
+    cu = workloads.random_layout(rng, T, 1, int(rng.integers(50, 1200)))
+    D = [64, 128][seed % 2]
+    hkv = int(rng.integers(1, 3))
+    hq = hkv * int(rng.integers(1, 5))
+    q, k, v, do = workloads.qkv_do(T, hq, hkv, D, seed=seed, dtype="bf16")
+    full_compare(q, k, v, do, cu, "bf16", scale=float(rng.uniform(0.05, 0.2)))
+
+
+def test_bf16_single_long_document_and_one_token_rows():
+    for cu in ([0, 3000], list(range(0, 257))):
+        cu = np.asarray(cu, dtype=np.int32)
+        T = int(cu[-1])
+        q, k, v, do = workloads.qkv_do(T, 4, 2, 128, seed=T, dtype="bf16")
+        full_compare(q, k, v, do, cu, "bf16")
+
+
+def test_bf16_packed_kv_views_match_contiguous():
+    # kv stacked as [T, 2, Hkv, D]: k = kv[:, 0], v = kv[:, 1] (token stride 2*Hkv*D)
+    cu = np.array([0, 100, 333, 700], dtype=np.int32)
+    T, hq, hkv, D = 700, 8, 2, 128
+    q, k, v, do = workloads.qkv_do(T, hq, hkv, D, seed=5, dtype="bf16")
+    dev = torch.device("cuda:0")
+    kv = torch.stack([k, v], dim=1).to(dev)
+    cud = torch.as_tensor(cu).to(dev)
+    qd, dod = q.to(dev), do.to(dev)
+    o1, l1 = psc.varlen_attn_fwd(qd, kv[:, 0], kv[:, 1], cud, 367)
+    g1 = psc.varlen_attn_bwd(qd, kv[:, 0], kv[:, 1], o1, dod, l1, cud, 367)
+    o2, l2 = psc.varlen_attn_fwd(qd, k.to(dev), v.to(dev), cud, 367)
+    g2 = psc.varlen_attn_bwd(qd, k.to(dev), v.to(dev), o2, dod, l2, cud, 367)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    for a, b in zip(g1, g2):
+        assert torch.equal(a, b)
+
+
+def test_bf16_repeat_is_bit_identical_and_guards_hold():
+    cu = np.concatenate([[0], np.cumsum(EDGE_LAYOUT)]).astype(np.int32)
+    T, hq, hkv, D = int(cu[-1]), 8, 2, 128
+    q, k, v, do = workloads.qkv_do(T, hq, hkv, D, seed=9, dtype="bf16")
+    dev = torch.device("cuda:0")
+    qd, kd, vd, dod = q.to(dev), k.to(dev), v.to(dev), do.to(dev)
+    cud = torch.as_tensor(cu).to(dev)
+    G = 4096  # guard elements on each side
+    sent = -12345.0
+
+    def guarded(n, dtype):
+        buf = torch.full((n + 2 * G,), sent, dtype=dtype, device=dev)
+        return buf, buf[G:G + n]
+
+    runs = []
+    for _ in range(2):
+        ob, o = guarded(T * hq * D, torch.bfloat16)
+        lb, l = guarded(hq * T, torch.float32)
+        qb, dq = guarded(T * hq * D, torch.float32)
+        kb, dk = guarded(T * hkv * D, torch.float32)
+        vb, dv = guarded(T * hkv * D, torch.float32)
+        o, l = o.view(T, hq, D), l.view(hq, T)
+        psc.varlen_attn_fwd(qd, kd, vd, cud, 431, out=o, lse=l)
+        psc.varlen_attn_bwd(qd, kd, vd, o, dod, l, cud, 431, dq=dq.view(T, hq, D), dk=dk.view(T, hkv, D),
+                            dv=dv.view(T, hkv, D))
+        torch.cuda.synchronize()
+        for buf in (ob, lb, qb, kb, vb):
+            assert (buf[:G].float() == sent).all() and (buf[-G:].float() == sent).all()
+        runs.append([x.clone() for x in (o, l, dq, dk, dv)])
+    for a, b in zip(*runs):
+        assert torch.equal(a, b)
+
+
+# ------------------------------------------------- full-size workloads
+
+def _layout(w):
+    if w.attn_cu_seqlens is not None:
+        return np.asarray(w.attn_cu_seqlens, dtype=np.int32)
+    p = w.pack
+    rows = pack_ref.build_pack(p.docs, p.micro_bsz, p.seq_len)[: p.keep_rows]
+    return np.asarray(pack_ref.flatten(rows, p.packed_length)["cu_seqlens"], dtype=np.int32)
+
+
+@pytest.mark.parametrize("name", ["uniform_8k", "lognormal_32k", "seqpar_share_128k", "skewed_32k"])
+def test_full_size_sampled(name):
+    w = workloads.make(name)
+    cu = _layout(w)
+    T = int(cu[-1])
+    a = w.attn
+    q, k, v, do = workloads.qkv_do(T, a.hq, a.hkv, a.head_dim, seed=0, dtype=a.dtype)
+    print(f"[{name}] T={T} segments={len(cu) - 1} hq={a.hq} hkv={a.hkv} D={a.head_dim}", flush=True)
+    got = run(q, k, v, do, cu, backward=a.backward)
+    rng = np.random.default_rng(1)
+    lens = np.diff(cu)
+    longest = int(np.argmax(lens))
+    s_long, e_long = int(cu[longest]), int(cu[longest + 1])
+    # random rows plus the tail of the longest document (its longest key ranges)
+    rows = np.concatenate([rng.integers(0, T, 96), np.arange(e_long - 32, e_long)])
+    heads = rng.integers(0, a.hq, rows.size)
+    o, lse = attn_ref.attn_rows(q, k, v, cu, rows, heads)
+    close("o", got["o"][rows, heads].numpy(), o, a.dtype)
+    close("lse", got["lse"][heads, rows].numpy(), lse, a.dtype)
+    if not a.backward:
+        return
+    dq = attn_ref.attn_rows_dq(q, k, v, do, cu, rows[:64], heads[:64])
+    close("dq", got["dq"][rows[:64], heads[:64]].numpy(), dq, a.dtype)
+    # dK/dV: the last keys of the longest document (one kv head), and two
+    # whole short documents (every kv head)
+    g = int(rng.integers(0, a.hkv))
+    key_lo = max(s_long, e_long - 160)
+    dk, dv = attn_ref.attn_bwd_keys(q, k, v, do, cu, longest, key_lo, [g])
+    close("dk tail", got["dk"][key_lo:e_long, [g]].numpy(), dk, a.dtype)
+    close("dv tail", got["dv"][key_lo:e_long, [g]].numpy(), dv, a.dtype)
+    short = [i for i in np.argsort(lens) if lens[i] > 8][:2]
+    heads_kv = list(range(a.hkv))
+    for si in short:
+        s, e = int(cu[si]), int(cu[si + 1])
+        dk, dv = attn_ref.attn_bwd_keys(q, k, v, do, cu, int(si), s, heads_kv)
+        close("dk doc", got["dk"][s:e].numpy(), dk, a.dtype)
+        close("dv doc", got["dv"][s:e].numpy(), dv, a.dtype)

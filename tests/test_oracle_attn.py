@@ -239,3 +239,17 @@ def test_element_sparsity_closed_form_and_half_row_bound():
     # tiles are empty
     cu = [0, 3, 7, 12, 16]
     assert abs(mask_stats.block_sparsity(cu, 4) - 10 / 16) < 1e-12
+
+
+def test_key_tail_gradients_match_full_oracle():
+    rng = np.random.default_rng(21)
+    T = 260
+    cu = np.array([0, 37, 200, 260], dtype=np.int32)
+    q, k, v, do = _inputs(T, 4, 2, 16, 21)
+    _, dk, dv = attn_ref.attn_bwd(q, k, v, do, cu)
+    for seg, key_lo in [(1, 150), (1, 37), (2, 259), (0, 10)]:
+        e = int(cu[seg + 1])
+        tk, tv = attn_ref.attn_bwd_keys(q, k, v, do, cu, seg, key_lo, [1, 0], block=23)
+        np.testing.assert_allclose(tk[:, 0], dk[key_lo:e, 1], atol=1e-13)
+        np.testing.assert_allclose(tk[:, 1], dk[key_lo:e, 0], atol=1e-13)
+        np.testing.assert_allclose(tv[:, 0], dv[key_lo:e, 1], atol=1e-13)

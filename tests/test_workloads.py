@@ -54,11 +54,12 @@ def test_skewed():
     cu = w.attn_cu_seqlens
     assert cu[-1] == 65536
     assert len(cu) - 1 == 982
-    assert w.attn_pad_segments == [24, 4]
     assert len(w.pack.docs) == 980
     L = np.diff(cu).astype(np.int64)
+    pad_idx = np.nonzero(w.attn_is_pad)[0]
+    assert L[pad_idx].tolist() == [24, 4]
+    assert [int(cu[i + 1]) for i in pad_idx] == [32768, 65536]
     # real tokens and in-document pairs exclude each row's padding segment
-    pad_idx = [i for i in range(len(L)) if cu[i + 1] in (32768, 65536)]
     real = L.sum() - L[pad_idx].sum()
     assert real == 65508
     tri_real = int((L * (L + 1) // 2).sum() - (L[pad_idx] * (L[pad_idx] + 1) // 2).sum())

@@ -32,7 +32,7 @@ MHA 64 x 64).
 from __future__ import annotations
 
 import math
-from dataclasses import dataclass, field
+from dataclasses import dataclass
 from typing import List, Optional
 
 import numpy as np
@@ -87,8 +87,9 @@ class Workload:
     # Attention layout given directly by the workload (tiny, skewed); None means
     # "the first keep_rows rows of the packer's output".
     attn_cu_seqlens: Optional[np.ndarray] = None
-    # Number of padding tokens in the directly given layout (last segment of a row).
-    attn_pad_segments: List[int] = field(default_factory=list)
+    # Per segment of the directly given layout: True where the segment is a
+    # row's zero-padded tail (computed like any segment, never counted as work).
+    attn_is_pad: Optional[np.ndarray] = None
 
 
 def _lognormal_len(rng, median, sigma, lo, hi):
@@ -172,18 +173,20 @@ def skewed_32k(seed: int = 0) -> Workload:
     docs = _ids(rng, lengths)
     # Attention layout: each row's documents, then its padding tail as the last
     # segment of the row.  Offsets are the running total of these lengths.
-    seg = []
+    seg, is_pad = [], []
     for row, pad in zip(per_row, pads):
         seg.extend(row)
+        is_pad.extend([False] * len(row))
         if pad:
             seg.append(pad)
+            is_pad.append(True)
     layout = np.zeros(len(seg) + 1, dtype=np.int32)
     layout[1:] = np.cumsum(seg)
     # The packer itself runs the literal truncate-and-pad rule over the same
     # document stream (micro_bsz 16, SEQ_LEN 2048).
     return Workload("skewed_32k", PackInput(docs, 16, 2048, BUILD_UNPACK),
                     AttnShape(64, 64, 64, "bf16", True), attn_cu_seqlens=layout,
-                    attn_pad_segments=[p for p in pads if p])
+                    attn_is_pad=np.array(is_pad, dtype=bool))
 
 
 WORKLOADS = {
