@@ -114,7 +114,9 @@ int psc_pack_sizes(int mode, int64_t n_docs, int64_t n_tokens, int32_t micro_bsz
  *                                           cu_seqlens[row_seg_ptr[r] .. row_seg_ptr[r+1]].
  *   row_valid_len int32 [n_rows] or NULL    tokens before the row's padding.
  *   stats        int32 [4]                  n_seg, max_seqlen (longest segment, padding
- *                                           included), rows_filled, 0.
+ *                                           included), rows_filled, and 1 if doc_offsets
+ *                                           broke its precondition so badly that the
+ *                                           segments overran max_segments (else 0).
  * Rows past rows_filled (only when build_unpack meets empty documents) hold
  * padding only and no segment.
  * Errors: PSC_ERR_INVALID (null pointer, sizes inconsistent with
