@@ -6,11 +6,21 @@
 // inside the document's causal triangle are visited and no mask is stored
 // ("Sample Packing：长序列 LLM 训练的 Attention 问题及优化", sections 三 and 5.1).
 //
+// Key/value blocks are double-buffered in LDS and filled with asynchronous
+// direct-to-LDS loads (global_load_lds_dwordx4): block j+1 streams in while
+// block j is computed, and no VGPR holds staging data.  Because each load
+// instruction writes 64 consecutive 16-byte LDS slots in lane order, the tile
+// layout is chosen by which global chunk each lane fetches: chunk c of row r
+// sits in slot c ^ swz(r) of that row (see lds_slot), which keeps both the
+// row reads of K and the column reads of V free of bank conflicts.
+//
 // Per 64-key block and wave (layouts in attn_common.h):
 //   S^T = K Q^T    A = K rows from LDS, B = Q kept in registers; each lane
 //                  then holds 32 scores of its own query row.
-//   online softmax in the exp2 domain (scale*log2(e) folded in), fp32 running
-//                  max (shared by the two lane halves) and per-lane partial sum.
+//   online softmax in the exp2 domain: raw-score max, one fma + exp2 per
+//                  score, and the running max is raised only when a row's max
+//                  grows by more than 2^8 (so O and l are rescaled rarely; the
+//                  result is exact either way, p just stays below 2^8).
 //   O^T += V^T P^T A = V read column-wise from LDS with ds_read_b64_tr_b16,
 //                  B = P rounded to bf16 straight from the score registers.
 // Epilogue: O / l in bf16, lse = (m + log2 l) * ln 2 in fp32.
@@ -23,12 +33,7 @@ namespace {
 constexpr int kBM = 128;  // query rows per workgroup
 constexpr int kBN = 64;   // keys per block
 constexpr int kThreads = 256;
-
-template <int D>
-struct FwdLds {
-  static constexpr int KS = D + 8;   // K row stride (elements)
-  static constexpr int VS = D + 16;  // V row stride (elements)
-};
+constexpr float kRescaleSlack = 8.0f;  // log2 units
 
 struct FwdParams {
   const bf16 *q, *k, *v;
@@ -43,10 +48,131 @@ struct FwdParams {
 };
 
 template <int D>
+struct Tile {
+  static constexpr int CPR = D / 8;          // 16-byte chunks per row
+  static constexpr int CHUNKS = kBN * CPR;   // chunks per K (or V) tile
+  static constexpr int LOADS = CHUNKS / 64;  // wave-wide load instructions per tile
+  static constexpr int LOADS_PER_WAVE = LOADS / (kThreads / 64);
+  static constexpr int BYTES = CHUNKS * 16;
+};
+
+// Slot of logical 16-byte chunk c of row r inside the row (XOR swizzle).
+template <int D>
+__device__ __forceinline__ int lds_slot(int r, int c) {
+  if constexpr (D == 128) return c ^ (((r & 7) << 1) | ((r >> 3) & 1));
+  else return c ^ (((r & 3) << 1) | ((r >> 2) & 1));
+}
+// Byte offset of element e (a multiple of 4) of row r.
+template <int D>
+__device__ __forceinline__ int lds_byte(int r, int e) {
+  return (r * Tile<D>::CPR + lds_slot<D>(r, e >> 3)) * 16 + (e & 7) * 2;
+}
+
+// Issue the asynchronous loads of key/value rows [kb, kb + 64) of the segment
+// into one LDS stage.  Rows past the segment end repeat its last row (their
+// scores are masked, so any finite data will do).
+template <int D>
+__device__ __forceinline__ void load_kv(const bf16* Kp, const bf16* Vp, int64_t sk, int64_t sv, int32_t kb,
+                                        int32_t L, bf16* Ks, bf16* Vs, int w, int l) {
+  using T_ = Tile<D>;
+#pragma unroll
+  for (int i = 0; i < T_::LOADS_PER_WAVE; ++i) {
+    const int t = w + 4 * i;          // load instruction index within the tile
+    const int slot = 64 * t + l;      // physical chunk this lane writes
+    const int r = slot / T_::CPR;
+    const int c = lds_slot<D>(r, slot % T_::CPR);  // the swizzle is an involution
+    const int32_t key = min(kb + r, L - 1);
+    __builtin_amdgcn_global_load_lds(Kp + (int64_t)key * sk + c * 8,
+                                     (PSC_LDS void*)(reinterpret_cast<char*>(Ks) + 64 * t * 16), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(Vp + (int64_t)key * sv + c * 8,
+                                     (PSC_LDS void*)(reinterpret_cast<char*>(Vs) + 64 * t * 16), 16, 0, 0);
+  }
+}
+
+template <int D>
+struct FwdState {
+  bf16x8 qf[D / 16];
+  f32x16 oacc[D / 32];
+  float m_i, l_i;
+};
+
+// One 64-key block for one wave.
+template <int D>
+__device__ __forceinline__ void fwd_block(FwdState<D>& st, const bf16* Ks, const bf16* Vs, int32_t kb, int32_t L,
+                                          int32_t qrow, int32_t wq_lo, float c2, int h, int lq, int l) {
+  const char* Kb = reinterpret_cast<const char*>(Ks);
+  const char* Vb = reinterpret_cast<const char*>(Vs);
+  f32x16 s[2];
+#pragma unroll
+  for (int n2 = 0; n2 < 2; ++n2) {
+    s[n2] = f32x16{};
+    const int r = 32 * n2 + lq;
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(Kb + lds_byte<D>(r, 16 * kk + 8 * h));
+      s[n2] = mfma32(a, st.qf[kk], s[n2]);
+    }
+  }
+  if ((kb + kBN - 1 > wq_lo) || (kb + kBN > L)) {
+#pragma unroll
+    for (int n2 = 0; n2 < 2; ++n2) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int32_t key = kb + 32 * n2 + 8 * (i >> 2) + 4 * h + (i & 3);
+        if (key > qrow || key >= L) s[n2][i] = -INFINITY;
+      }
+    }
+  }
+  float mx = s[0][0];
+#pragma unroll
+  for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[0][i]);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[1][i]);
+  mx = max_halves(mx) * c2;
+  // raise the running max only when this block's max exceeds it by > 2^8
+  if (__builtin_amdgcn_ballot_w64(mx > st.m_i + kRescaleSlack) != 0) {
+    const float m_new = fmaxf(st.m_i, mx);
+    const float alpha = fast_exp2(st.m_i - m_new);
+    st.l_i *= alpha;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) st.oacc[dt] *= alpha;
+    st.m_i = m_new;
+  }
+  const float neg_m = -st.m_i;
+  float rs = 0.f;
+  bf16x8 pb[4];
+#pragma unroll
+  for (int n2 = 0; n2 < 2; ++n2) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float e = fast_exp2(__builtin_fmaf(s[n2][i], c2, neg_m));
+      rs += e;
+      pb[2 * n2 + (i >> 3)][i & 7] = (bf16)e;
+    }
+  }
+  st.l_i += rs;
+  const int gi = l & 15;
+  const int dsub = 16 * ((l >> 4) & 1);
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) {
+    const int col = 32 * dt + dsub + 4 * (gi & 3);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int r0 = 16 * ks + 4 * h + (gi >> 2);
+      const bf16* p0 = reinterpret_cast<const bf16*>(Vb + lds_byte<D>(r0, col));
+      const bf16* p1 = reinterpret_cast<const bf16*>(Vb + lds_byte<D>(r0 + 8, col));
+      st.oacc[dt] = mfma32(tr_read8(p0, p1), pb[ks], st.oacc[dt]);
+    }
+  }
+}
+
+template <int D>
 __global__ void __launch_bounds__(kThreads, 2) k_attn_fwd(FwdParams p) {
-  using L_ = FwdLds<D>;
-  __shared__ __attribute__((aligned(16))) bf16 Ks[kBN * L_::KS];
-  __shared__ __attribute__((aligned(16))) bf16 Vs[kBN * L_::VS];
+  using T_ = Tile<D>;
+  __shared__ __attribute__((aligned(16))) bf16 Ks0[T_::BYTES / 2];
+  __shared__ __attribute__((aligned(16))) bf16 Vs0[T_::BYTES / 2];
+  __shared__ __attribute__((aligned(16))) bf16 Ks1[T_::BYTES / 2];
+  __shared__ __attribute__((aligned(16))) bf16 Vs1[T_::BYTES / 2];
 
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, h = l >> 5, lq = l & 31;
   const uint32_t b = xcd_group_remap(blockIdx.x, gridDim.x, (uint32_t)p.group);
@@ -65,108 +191,40 @@ __global__ void __launch_bounds__(kThreads, 2) k_attn_fwd(FwdParams p) {
   const bf16* Kp = p.k + (int64_t)s0 * p.sk + (int64_t)kvh * D;
   const bf16* Vp = p.v + (int64_t)s0 * p.sv + (int64_t)kvh * D;
 
-  const int32_t qrow = q0 + 32 * w + lq;
-  const bool qvalid = qrow < L;
-  bf16x8 qf[D / 16];
-#pragma unroll
-  for (int kk = 0; kk < D / 16; ++kk) {
-    qf[kk] = qvalid ? *reinterpret_cast<const bf16x8*>(Qp + (int64_t)qrow * p.sq + 16 * kk + 8 * h)
-                    : bf16x8{};
-  }
-
-  float m_i = -INFINITY, l_i = 0.f;
-  f32x16 oacc[D / 32];
-#pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt) oacc[dt] = f32x16{};
-
   const int32_t kv_end = min(q0 + kBM, L);
   const int32_t nkv = (kv_end + kBN - 1) / kBN;
+  load_kv<D>(Kp, Vp, p.sk, p.sv, 0, L, Ks0, Vs0, w, l);
+
+  const int32_t qrow = q0 + 32 * w + lq;
+  const bool qvalid = qrow < L;
+  FwdState<D> st;
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk) {
+    st.qf[kk] = qvalid ? *reinterpret_cast<const bf16x8*>(Qp + (int64_t)qrow * p.sq + 16 * kk + 8 * h)
+                       : bf16x8{};
+  }
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) st.oacc[dt] = f32x16{};
+  st.m_i = -INFINITY;
+  st.l_i = 0.f;
+
   const int32_t wq_lo = q0 + 32 * w, wq_hi = wq_lo + 31;
-  const int gi = l & 15;
-  const int dsub = 16 * ((l >> 4) & 1);
-
-  for (int32_t j = 0; j < nkv; ++j) {
-    const int32_t kb = j * kBN;
+  const float c2 = p.scale_log2;
+  for (int32_t j = 0; j < nkv; j += 2) {
+    // stage 0 holds block j
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    constexpr int CH = D / 8;  // 16-byte chunks per row
-#pragma unroll
-    for (int c = tid; c < kBN * CH; c += kThreads) {
-      const int r = c / CH, cc = c % CH;
-      const int32_t key = kb + r;
-      bf16x8 kv = {}, vv = {};
-      if (key < L) {
-        kv = *reinterpret_cast<const bf16x8*>(Kp + (int64_t)key * p.sk + cc * 8);
-        vv = *reinterpret_cast<const bf16x8*>(Vp + (int64_t)key * p.sv + cc * 8);
-      }
-      *reinterpret_cast<bf16x8*>(&Ks[r * L_::KS + cc * 8]) = kv;
-      *reinterpret_cast<bf16x8*>(&Vs[r * L_::VS + cc * 8]) = vv;
-    }
+    if (j + 1 < nkv) load_kv<D>(Kp, Vp, p.sk, p.sv, (j + 1) * kBN, L, Ks1, Vs1, w, l);
+    if (j * kBN <= wq_hi) fwd_block<D>(st, Ks0, Vs0, j * kBN, L, qrow, wq_lo, c2, h, lq, l);
+    if (j + 1 >= nkv) break;
+    // stage 1 holds block j + 1
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (kb > wq_hi) continue;  // block entirely above this wave's rows
-
-    f32x16 s[2];
-#pragma unroll
-    for (int n2 = 0; n2 < 2; ++n2) {
-      s[n2] = f32x16{};
-#pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&Ks[(32 * n2 + lq) * L_::KS + 16 * kk + 8 * h]);
-        s[n2] = mfma32(a, qf[kk], s[n2]);
-      }
-    }
-
-    const bool need_mask = (kb + kBN - 1 > wq_lo) || (kb + kBN > L);
-    float mx = -INFINITY;
-#pragma unroll
-    for (int n2 = 0; n2 < 2; ++n2) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float x = s[n2][i] * p.scale_log2;
-        if (need_mask) {
-          const int32_t key = kb + 32 * n2 + 8 * (i >> 2) + 4 * h + (i & 3);
-          if (key > qrow || key >= L) x = -INFINITY;
-        }
-        s[n2][i] = x;
-        mx = fmaxf(mx, x);
-      }
-    }
-    mx = max_halves(mx);
-    const float m_new = fmaxf(m_i, mx);
-    const float alpha = fast_exp2(m_i - m_new);
-    float rs = 0.f;
-#pragma unroll
-    for (int n2 = 0; n2 < 2; ++n2) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float e = fast_exp2(s[n2][i] - m_new);
-        s[n2][i] = e;
-        rs += e;
-      }
-    }
-    l_i = l_i * alpha + rs;
-    m_i = m_new;
-#pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt) oacc[dt] *= alpha;
-
-    bf16x8 pb[4];
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-#pragma unroll
-      for (int jj = 0; jj < 8; ++jj) pb[ks][jj] = (bf16)s[ks >> 1][8 * (ks & 1) + jj];
-    }
-#pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt) {
-      const int col = 32 * dt + dsub + 4 * (gi & 3);
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const bf16* p0 = &Vs[(16 * ks + 4 * h + (gi >> 2)) * L_::VS + col];
-        const bf16x8 a = tr_read8(p0, p0 + 8 * L_::VS);
-        oacc[dt] = mfma32(a, pb[ks], oacc[dt]);
-      }
-    }
+    if (j + 2 < nkv) load_kv<D>(Kp, Vp, p.sk, p.sv, (j + 2) * kBN, L, Ks0, Vs0, w, l);
+    if ((j + 1) * kBN <= wq_hi) fwd_block<D>(st, Ks1, Vs1, (j + 1) * kBN, L, qrow, wq_lo, c2, h, lq, l);
   }
 
-  const float lt = sum_halves(l_i);
+  const float lt = sum_halves(st.l_i);
   if (qvalid) {
     const float inv = 1.f / lt;
     bf16* Op = p.out + (int64_t)(s0 + qrow) * p.so + (int64_t)head * D;
@@ -176,11 +234,11 @@ __global__ void __launch_bounds__(kThreads, 2) k_attn_fwd(FwdParams p) {
       for (int g4 = 0; g4 < 4; ++g4) {
         bf16x4 o4;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) o4[e] = (bf16)(oacc[dt][4 * g4 + e] * inv);
+        for (int e = 0; e < 4; ++e) o4[e] = (bf16)(st.oacc[dt][4 * g4 + e] * inv);
         *reinterpret_cast<bf16x4*>(Op + 32 * dt + 8 * g4 + 4 * h) = o4;
       }
     }
-    if (h == 0) p.lse[(int64_t)head * p.T + s0 + qrow] = (m_i + __log2f(lt)) * kLn2;
+    if (h == 0) p.lse[(int64_t)head * p.T + s0 + qrow] = (st.m_i + __log2f(lt)) * kLn2;
   }
 }
 
