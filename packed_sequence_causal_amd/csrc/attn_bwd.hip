@@ -2,8 +2,8 @@
 //
 // Gradients of sum(dO * O) for O = softmax(scale * Q K^T restricted to each
 // document's causal triangle) V, with P recomputed from the forward's lse:
-//   D_i   = <dO_i, O_i>                      (k_bwd_pre)
-//   P     = exp(scale * q_i.k_j - lse_i)      (recomputed)
+//   D_i   = <dO_i, O_i>                      (k_bwd_pre, with lse_i * log2 e)
+//   P     = exp(scale * q_i.k_j - lse_i)      (recomputed, exp2 domain)
 //   dP    = dO V^T,   dS = P * (dP - D)
 //   dV    = P^T dO,   dK = scale dS^T Q       (k_bwd_dkdv: one workgroup per
 //                                              128-key tile and key/value head;
@@ -18,6 +18,10 @@
 // every output element is written once, and results are deterministic.
 // Both loops visit only tiles inside a document's causal triangle ("Sample
 // Packing：长序列 LLM 训练的 Attention 问题及优化", section 5.1).
+//
+// The streamed operand of each kernel (K/V blocks for dQ, Q/dO blocks plus
+// their lse and D for dK/dV) is double-buffered in LDS and filled with
+// asynchronous direct-to-LDS loads, as in the forward (attn_common.h).
 #include "attn_common.h"
 #include "psc_internal.h"
 
@@ -33,7 +37,8 @@ constexpr int kBMk = 64;   // dK/dV kernel: queries per block
 struct BwdParams {
   const bf16 *q, *k, *v, *o, *dout;
   const float* lse;
-  float* Dbuf;  // [hq][T]
+  float* Dbuf;   // [hq][T]  D_i
+  float* L2buf;  // [hq][T]  lse_i * log2(e)
   float *dq, *dk, *dv;
   int64_t sq, sk, sv, so, sdo, T;
   const int32_t* cu;
@@ -43,43 +48,112 @@ struct BwdParams {
   float scale, scale_log2;
 };
 
-// D[h][t] = sum_d dO[t,h,d] * O[t,h,d] in fp32; 16 lanes per (token, head)
-// for D = 128 (8 per lane), 8 lanes for D = 64.
+// D[h][t] = sum_d dO[t,h,d] * O[t,h,d] and L2[h][t] = lse[h][t] * log2(e).
+// One workgroup = 64 tokens of one head; D/8 lanes read one row (coalesced),
+// the 64 results are written as one contiguous run.
 template <int D>
 __global__ void __launch_bounds__(kThreads) k_bwd_pre(BwdParams p) {
-  constexpr int LPR = D / 8;  // lanes per row
-  const int64_t gid = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  const int64_t row = gid / LPR;  // row = t * hq + h
-  const int part = (int)(gid % LPR);
-  float acc = 0.f;
-  if (row < p.T * p.hq) {
-    const int64_t t = row / p.hq;
-    const int h = (int)(row % p.hq);
-    const bf16x8 a = *reinterpret_cast<const bf16x8*>(p.o + t * p.so + (int64_t)h * D + part * 8);
-    const bf16x8 b = *reinterpret_cast<const bf16x8*>(p.dout + t * p.sdo + (int64_t)h * D + part * 8);
+  constexpr int LPR = D / 8;             // lanes per row
+  constexpr int RPP = kThreads / LPR;    // rows per pass
+  __shared__ float res[64];
+  const int h = blockIdx.y;
+  const int64_t t0 = (int64_t)blockIdx.x * 64;
+  const int part = threadIdx.x % LPR;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc += (float)a[e] * (float)b[e];
+  for (int pass = 0; pass < 64 / RPP; ++pass) {
+    const int r = pass * RPP + threadIdx.x / LPR;
+    const int64_t t = t0 + r;
+    float acc = 0.f;
+    if (t < p.T) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(p.o + t * p.so + (int64_t)h * D + part * 8);
+      const bf16x8 b = *reinterpret_cast<const bf16x8*>(p.dout + t * p.sdo + (int64_t)h * D + part * 8);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc = __builtin_fmaf((float)a[e], (float)b[e], acc);
+    }
+#pragma unroll
+    for (int o = LPR / 2; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
+    if (part == 0) res[r] = acc;
   }
+  __syncthreads();
+  if (threadIdx.x < 64) {
+    const int64_t t = t0 + threadIdx.x;
+    if (t < p.T) {
+      p.Dbuf[(int64_t)h * p.T + t] = res[threadIdx.x];
+      p.L2buf[(int64_t)h * p.T + t] = p.lse[(int64_t)h * p.T + t] * kLog2e;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------- dQ
+
+template <int D>
+struct DqState {
+  bf16x8 qf[D / 16], df[D / 16];
+  f32x16 acc[D / 32];
+  float lse2, Drow;
+};
+
+// One 64-key block of the dQ loop for one wave.
+template <int D>
+__device__ __forceinline__ void dq_block(DqState<D>& st, const bf16* Ks, const bf16* Vs, int32_t kb, int32_t L,
+                                         int32_t qrow, int32_t wq_lo, float c2, int h, int lq, int l) {
+  const char* Kb = reinterpret_cast<const char*>(Ks);
+  const char* Vb = reinterpret_cast<const char*>(Vs);
+  f32x16 s[2], dp[2];
 #pragma unroll
-  for (int o = LPR / 2; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
-  if (row < p.T * p.hq && part == 0) {
-    const int64_t t = row / p.hq;
-    const int h = (int)(row % p.hq);
-    p.Dbuf[(int64_t)h * p.T + t] = acc;
+  for (int n2 = 0; n2 < 2; ++n2) {
+    s[n2] = f32x16{};
+    dp[n2] = f32x16{};
+    const int r = 32 * n2 + lq;
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+      const bf16x8 ak = *reinterpret_cast<const bf16x8*>(Kb + lds_byte<D>(r, 16 * kk + 8 * h));
+      const bf16x8 av = *reinterpret_cast<const bf16x8*>(Vb + lds_byte<D>(r, 16 * kk + 8 * h));
+      s[n2] = mfma32(ak, st.qf[kk], s[n2]);
+      dp[n2] = mfma32(av, st.df[kk], dp[n2]);
+    }
+  }
+  if ((kb + kBNq - 1 > wq_lo) || (kb + kBNq > L)) {
+#pragma unroll
+    for (int n2 = 0; n2 < 2; ++n2) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int32_t key = kb + 32 * n2 + 8 * (i >> 2) + 4 * h + (i & 3);
+        if (key > qrow || key >= L) s[n2][i] = -INFINITY;
+      }
+    }
+  }
+  const float neg_l = -st.lse2;
+  bf16x8 dsb[4];
+#pragma unroll
+  for (int n2 = 0; n2 < 2; ++n2) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float pr = fast_exp2(__builtin_fmaf(s[n2][i], c2, neg_l));
+      dsb[2 * n2 + (i >> 3)][i & 7] = (bf16)(pr * (dp[n2][i] - st.Drow));
+    }
+  }
+  const int gi = l & 15;
+  const int dsub = 16 * ((l >> 4) & 1);
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) {
+    const int col = 32 * dt + dsub + 4 * (gi & 3);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int r0 = 16 * ks + 4 * h + (gi >> 2);
+      const bf16* p0 = reinterpret_cast<const bf16*>(Kb + lds_byte<D>(r0, col));
+      const bf16* p1 = reinterpret_cast<const bf16*>(Kb + lds_byte<D>(r0 + 8, col));
+      st.acc[dt] = mfma32(tr_read8(p0, p1), dsb[ks], st.acc[dt]);
+    }
   }
 }
 
 template <int D>
-struct KSt {
-  static constexpr int S = D + 8;
-};
-
-// ---------------------------------------------------------------------- dQ
-template <int D>
 __global__ void __launch_bounds__(kThreads, 2) k_bwd_dq(BwdParams p) {
-  constexpr int S = KSt<D>::S;
-  __shared__ __attribute__((aligned(16))) bf16 Ks[kBNq * S];
-  __shared__ __attribute__((aligned(16))) bf16 Vs[kBNq * S];
+  __shared__ __attribute__((aligned(16))) bf16 Ks0[kBNq * D];
+  __shared__ __attribute__((aligned(16))) bf16 Vs0[kBNq * D];
+  __shared__ __attribute__((aligned(16))) bf16 Ks1[kBNq * D];
+  __shared__ __attribute__((aligned(16))) bf16 Vs1[kBNq * D];
 
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, h = l >> 5, lq = l & 31;
   const uint32_t b = xcd_group_remap(blockIdx.x, gridDim.x, (uint32_t)p.group);
@@ -94,89 +168,46 @@ __global__ void __launch_bounds__(kThreads, 2) k_bwd_dq(BwdParams p) {
 
   const bf16* Kp = p.k + (int64_t)s0 * p.sk + (int64_t)kvh * D;
   const bf16* Vp = p.v + (int64_t)s0 * p.sv + (int64_t)kvh * D;
+  const int32_t kv_end = min(q0 + kBQ, L);
+  const int32_t nkv = (kv_end + kBNq - 1) / kBNq;
+  load_tile_async<D, kBNq, kThreads / 64>(Kp, p.sk, 0, L, Ks0, w, l);
+  load_tile_async<D, kBNq, kThreads / 64>(Vp, p.sv, 0, L, Vs0, w, l);
 
   const int32_t qrow = q0 + 32 * w + lq;
   const bool qvalid = qrow < L;
-  bf16x8 qf[D / 16], df[D / 16];
+  DqState<D> st;
   {
     const bf16* Qr = p.q + (int64_t)(s0 + qrow) * p.sq + (int64_t)head * D;
     const bf16* Dr = p.dout + (int64_t)(s0 + qrow) * p.sdo + (int64_t)head * D;
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) {
-      qf[kk] = qvalid ? *reinterpret_cast<const bf16x8*>(Qr + 16 * kk + 8 * h) : bf16x8{};
-      df[kk] = qvalid ? *reinterpret_cast<const bf16x8*>(Dr + 16 * kk + 8 * h) : bf16x8{};
+      st.qf[kk] = qvalid ? *reinterpret_cast<const bf16x8*>(Qr + 16 * kk + 8 * h) : bf16x8{};
+      st.df[kk] = qvalid ? *reinterpret_cast<const bf16x8*>(Dr + 16 * kk + 8 * h) : bf16x8{};
     }
   }
-  const float lse2 = qvalid ? p.lse[(int64_t)head * p.T + s0 + qrow] * kLog2e : 0.f;
-  const float Drow = qvalid ? p.Dbuf[(int64_t)head * p.T + s0 + qrow] : 0.f;
-
-  f32x16 acc[D / 32];
+  st.lse2 = qvalid ? p.L2buf[(int64_t)head * p.T + s0 + qrow] : 0.f;
+  st.Drow = qvalid ? p.Dbuf[(int64_t)head * p.T + s0 + qrow] : 0.f;
 #pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt) acc[dt] = f32x16{};
+  for (int dt = 0; dt < D / 32; ++dt) st.acc[dt] = f32x16{};
 
-  const int32_t kv_end = min(q0 + kBQ, L);
-  const int32_t nkv = (kv_end + kBNq - 1) / kBNq;
   const int32_t wq_lo = q0 + 32 * w, wq_hi = wq_lo + 31;
-  const int gi = l & 15;
-  const int dsub = 16 * ((l >> 4) & 1);
-
-  for (int32_t j = 0; j < nkv; ++j) {
-    const int32_t kb = j * kBNq;
+  const float c2 = p.scale_log2;
+  for (int32_t j = 0; j < nkv; j += 2) {
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    constexpr int CH = D / 8;
-#pragma unroll
-    for (int c = tid; c < kBNq * CH; c += kThreads) {
-      const int r = c / CH, cc = c % CH;
-      const int32_t key = kb + r;
-      bf16x8 kv = {}, vv = {};
-      if (key < L) {
-        kv = *reinterpret_cast<const bf16x8*>(Kp + (int64_t)key * p.sk + cc * 8);
-        vv = *reinterpret_cast<const bf16x8*>(Vp + (int64_t)key * p.sv + cc * 8);
-      }
-      *reinterpret_cast<bf16x8*>(&Ks[r * S + cc * 8]) = kv;
-      *reinterpret_cast<bf16x8*>(&Vs[r * S + cc * 8]) = vv;
+    if (j + 1 < nkv) {
+      load_tile_async<D, kBNq, kThreads / 64>(Kp, p.sk, (j + 1) * kBNq, L, Ks1, w, l);
+      load_tile_async<D, kBNq, kThreads / 64>(Vp, p.sv, (j + 1) * kBNq, L, Vs1, w, l);
     }
+    if (j * kBNq <= wq_hi) dq_block<D>(st, Ks0, Vs0, j * kBNq, L, qrow, wq_lo, c2, h, lq, l);
+    if (j + 1 >= nkv) break;
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (kb > wq_hi) continue;
-
-    f32x16 s[2], dp[2];
-#pragma unroll
-    for (int n2 = 0; n2 < 2; ++n2) {
-      s[n2] = f32x16{};
-      dp[n2] = f32x16{};
-#pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk) {
-        const bf16x8 ak = *reinterpret_cast<const bf16x8*>(&Ks[(32 * n2 + lq) * S + 16 * kk + 8 * h]);
-        const bf16x8 av = *reinterpret_cast<const bf16x8*>(&Vs[(32 * n2 + lq) * S + 16 * kk + 8 * h]);
-        s[n2] = mfma32(ak, qf[kk], s[n2]);
-        dp[n2] = mfma32(av, df[kk], dp[n2]);
-      }
+    if (j + 2 < nkv) {
+      load_tile_async<D, kBNq, kThreads / 64>(Kp, p.sk, (j + 2) * kBNq, L, Ks0, w, l);
+      load_tile_async<D, kBNq, kThreads / 64>(Vp, p.sv, (j + 2) * kBNq, L, Vs0, w, l);
     }
-    const bool need_mask = (kb + kBNq - 1 > wq_lo) || (kb + kBNq > L);
-    bf16x8 dsb[4];
-#pragma unroll
-    for (int n2 = 0; n2 < 2; ++n2) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float pr = fast_exp2(s[n2][i] * p.scale_log2 - lse2);
-        if (need_mask) {
-          const int32_t key = kb + 32 * n2 + 8 * (i >> 2) + 4 * h + (i & 3);
-          if (key > qrow || key >= L) pr = 0.f;
-        }
-        const float ds = pr * (dp[n2][i] - Drow);
-        dsb[2 * n2 + (i >> 3)][i & 7] = (bf16)ds;
-      }
-    }
-#pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt) {
-      const int col = 32 * dt + dsub + 4 * (gi & 3);
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const bf16* p0 = &Ks[(16 * ks + 4 * h + (gi >> 2)) * S + col];
-        const bf16x8 a = tr_read8(p0, p0 + 8 * S);
-        acc[dt] = mfma32(a, dsb[ks], acc[dt]);
-      }
-    }
+    if ((j + 1) * kBNq <= wq_hi) dq_block<D>(st, Ks1, Vs1, (j + 1) * kBNq, L, qrow, wq_lo, c2, h, lq, l);
   }
 
   if (qvalid) {
@@ -187,7 +218,7 @@ __global__ void __launch_bounds__(kThreads, 2) k_bwd_dq(BwdParams p) {
       for (int g4 = 0; g4 < 4; ++g4) {
         f32x4 v4;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v4[e] = acc[dt][4 * g4 + e] * p.scale;
+        for (int e = 0; e < 4; ++e) v4[e] = st.acc[dt][4 * g4 + e] * p.scale;
         *reinterpret_cast<f32x4*>(Qd + 32 * dt + 8 * g4 + 4 * h) = v4;
       }
     }
@@ -195,13 +226,84 @@ __global__ void __launch_bounds__(kThreads, 2) k_bwd_dq(BwdParams p) {
 }
 
 // ------------------------------------------------------------------ dK, dV
+
+template <int D>
+struct DkvState {
+  bf16x8 kf[D / 16], vf[D / 16];
+  f32x16 dka[D / 32], dva[D / 32];
+};
+
+// One 64-query block of the dK/dV loop for one wave (keys wk_lo .. wk_lo+31,
+// this lane's key `key`).
+template <int D>
+__device__ __forceinline__ void dkdv_block(DkvState<D>& st, const bf16* Qs, const bf16* dOs, const float* l2s,
+                                           const float* Ds, int32_t qs, int32_t L, int32_t key, int32_t wk_lo,
+                                           float c2, int h, int lq, int l) {
+  const char* Qb = reinterpret_cast<const char*>(Qs);
+  const char* Ob = reinterpret_cast<const char*>(dOs);
+  const int gi = l & 15;
+  const int dsub = 16 * ((l >> 4) & 1);
+#pragma unroll
+  for (int mq = 0; mq < 2; ++mq) {
+    const int32_t qm = qs + 32 * mq;
+    if (qm + 31 < wk_lo) continue;  // every query of this half precedes every key of the wave
+    f32x16 s = {}, dp = {};
+    const int r = 32 * mq + lq;
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+      const bf16x8 aq = *reinterpret_cast<const bf16x8*>(Qb + lds_byte<D>(r, 16 * kk + 8 * h));
+      const bf16x8 ad = *reinterpret_cast<const bf16x8*>(Ob + lds_byte<D>(r, 16 * kk + 8 * h));
+      s = mfma32(aq, st.kf[kk], s);
+      dp = mfma32(ad, st.vf[kk], dp);
+    }
+    // s[i], dp[i] <-> query 32*mq + 8*(i/4) + 4*h + i%4 of the block, key = this lane's key
+    if ((qm < wk_lo + 31) || (qm + 32 > L)) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int32_t qa = qm + 8 * (i >> 2) + 4 * h + (i & 3);
+        if (qa < key || qa >= L) s[i] = -INFINITY;
+      }
+    }
+    bf16x8 pa[2], da[2];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const f32x4 l4 = *reinterpret_cast<const f32x4*>(l2s + 32 * mq + 8 * g + 4 * h);
+      const f32x4 d4 = *reinterpret_cast<const f32x4*>(Ds + 32 * mq + 8 * g + 4 * h);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = 4 * g + e;
+        const float pr = fast_exp2(__builtin_fmaf(s[i], c2, -l4[e]));
+        pa[i >> 3][i & 7] = (bf16)pr;
+        da[i >> 3][i & 7] = (bf16)(pr * (dp[i] - d4[e]));
+      }
+    }
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) {
+      const int col = 32 * dt + dsub + 4 * (gi & 3);
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const int r0 = 32 * mq + 16 * ks + 4 * h + (gi >> 2);
+        const bf16x8 bo = tr_read8(reinterpret_cast<const bf16*>(Ob + lds_byte<D>(r0, col)),
+                                   reinterpret_cast<const bf16*>(Ob + lds_byte<D>(r0 + 8, col)));
+        const bf16x8 bq = tr_read8(reinterpret_cast<const bf16*>(Qb + lds_byte<D>(r0, col)),
+                                   reinterpret_cast<const bf16*>(Qb + lds_byte<D>(r0 + 8, col)));
+        st.dva[dt] = mfma32(pa[ks], bo, st.dva[dt]);
+        st.dka[dt] = mfma32(da[ks], bq, st.dka[dt]);
+      }
+    }
+  }
+}
+
 template <int D>
 __global__ void __launch_bounds__(kThreads, 1) k_bwd_dkdv(BwdParams p) {
-  constexpr int S = KSt<D>::S;
-  __shared__ __attribute__((aligned(16))) bf16 Qs[kBMk * S];
-  __shared__ __attribute__((aligned(16))) bf16 dOs[kBMk * S];
-  __shared__ float lse_s[kBMk];
-  __shared__ float D_s[kBMk];
+  __shared__ __attribute__((aligned(16))) bf16 Qs0[kBMk * D];
+  __shared__ __attribute__((aligned(16))) bf16 dOs0[kBMk * D];
+  __shared__ __attribute__((aligned(16))) bf16 Qs1[kBMk * D];
+  __shared__ __attribute__((aligned(16))) bf16 dOs1[kBMk * D];
+  __shared__ __attribute__((aligned(16))) float l2s0[kBMk];
+  __shared__ __attribute__((aligned(16))) float Ds0[kBMk];
+  __shared__ __attribute__((aligned(16))) float l2s1[kBMk];
+  __shared__ __attribute__((aligned(16))) float Ds1[kBMk];
 
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, h = l >> 5, lq = l & 31;
   const uint32_t item = blockIdx.x / (uint32_t)p.hkv, kvh = blockIdx.x % (uint32_t)p.hkv;
@@ -214,103 +316,57 @@ __global__ void __launch_bounds__(kThreads, 1) k_bwd_dkdv(BwdParams p) {
   const int32_t key = kb + 32 * w + lq;  // this lane's key (S layout: lane <-> key)
   const bool kvalid = key < L;
   const int32_t wk_lo = kb + 32 * w;
+  const int32_t nqb = (L - kb + kBMk - 1) / kBMk;
+  const int32_t niter = p.group * nqb;
 
-  bf16x8 kf[D / 16], vf[D / 16];
+  // iteration t: query head kvh*G + t / nqb, query block kb + (t % nqb) * 64
+  auto issue = [&](int32_t t, bf16* Qs, bf16* dOs, float* l2s, float* Ds) {
+    const int32_t head = kvh * p.group + t / nqb;
+    const int32_t qs = kb + (t % nqb) * kBMk;
+    load_tile_async<D, kBMk, kThreads / 64>(p.q + (int64_t)s0 * p.sq + (int64_t)head * D, p.sq, qs, L, Qs, w, l);
+    load_tile_async<D, kBMk, kThreads / 64>(p.dout + (int64_t)s0 * p.sdo + (int64_t)head * D, p.sdo, qs, L, dOs,
+                                           w, l);
+    if (w == 0) load_vec64_async(p.L2buf + (int64_t)head * p.T + s0, qs, L, l2s, l);
+    if (w == 1) load_vec64_async(p.Dbuf + (int64_t)head * p.T + s0, qs, L, Ds, l);
+  };
+  issue(0, Qs0, dOs0, l2s0, Ds0);
+
+  DkvState<D> st;
   {
     const bf16* Kr = p.k + (int64_t)(s0 + key) * p.sk + (int64_t)kvh * D;
     const bf16* Vr = p.v + (int64_t)(s0 + key) * p.sv + (int64_t)kvh * D;
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) {
-      kf[kk] = kvalid ? *reinterpret_cast<const bf16x8*>(Kr + 16 * kk + 8 * h) : bf16x8{};
-      vf[kk] = kvalid ? *reinterpret_cast<const bf16x8*>(Vr + 16 * kk + 8 * h) : bf16x8{};
+      st.kf[kk] = kvalid ? *reinterpret_cast<const bf16x8*>(Kr + 16 * kk + 8 * h) : bf16x8{};
+      st.vf[kk] = kvalid ? *reinterpret_cast<const bf16x8*>(Vr + 16 * kk + 8 * h) : bf16x8{};
     }
   }
-  f32x16 dka[D / 32], dva[D / 32];
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) {
-    dka[dt] = f32x16{};
-    dva[dt] = f32x16{};
+    st.dka[dt] = f32x16{};
+    st.dva[dt] = f32x16{};
   }
-  const int gi = l & 15;
-  const int dsub = 16 * ((l >> 4) & 1);
-  const int32_t nqb = (L - kb + kBMk - 1) / kBMk;
+  const float c2 = p.scale_log2;
 
-  for (int32_t hh = 0; hh < p.group; ++hh) {
-    const int32_t head = kvh * p.group + hh;
-    const bf16* Qp = p.q + (int64_t)s0 * p.sq + (int64_t)head * D;
-    const bf16* Op = p.dout + (int64_t)s0 * p.sdo + (int64_t)head * D;
-    const float* lse_h = p.lse + (int64_t)head * p.T + s0;
-    const float* D_h = p.Dbuf + (int64_t)head * p.T + s0;
-    for (int32_t qb = 0; qb < nqb; ++qb) {
-      const int32_t qs = kb + qb * kBMk;
-      __syncthreads();
-      constexpr int CH = D / 8;
-#pragma unroll
-      for (int c = tid; c < kBMk * CH; c += kThreads) {
-        const int r = c / CH, cc = c % CH;
-        const int32_t qi = qs + r;
-        bf16x8 a = {}, bb = {};
-        if (qi < L) {
-          a = *reinterpret_cast<const bf16x8*>(Qp + (int64_t)qi * p.sq + cc * 8);
-          bb = *reinterpret_cast<const bf16x8*>(Op + (int64_t)qi * p.sdo + cc * 8);
-        }
-        *reinterpret_cast<bf16x8*>(&Qs[r * S + cc * 8]) = a;
-        *reinterpret_cast<bf16x8*>(&dOs[r * S + cc * 8]) = bb;
-      }
-      if (tid < kBMk) {
-        const int32_t qi = qs + tid;
-        lse_s[tid] = qi < L ? lse_h[qi] * kLog2e : 0.f;
-        D_s[tid] = qi < L ? D_h[qi] : 0.f;
-      }
-      __syncthreads();
-      if (qs + kBMk - 1 < wk_lo) continue;  // every query of the block precedes every key of this wave
-
-#pragma unroll
-      for (int mq = 0; mq < 2; ++mq) {
-        const int32_t qm = qs + 32 * mq;
-        if (qm + 31 < wk_lo) continue;
-        f32x16 s = {}, dp = {};
-#pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk) {
-          const bf16x8 aq = *reinterpret_cast<const bf16x8*>(&Qs[(32 * mq + lq) * S + 16 * kk + 8 * h]);
-          const bf16x8 ad = *reinterpret_cast<const bf16x8*>(&dOs[(32 * mq + lq) * S + 16 * kk + 8 * h]);
-          s = mfma32(aq, kf[kk], s);
-          dp = mfma32(ad, vf[kk], dp);
-        }
-        // s[i], dp[i] <-> query 32*mq + 8*(i/4) + 4*h + i%4 of the block, key = this lane's key
-        const bool need_mask = (qm < wk_lo + 31) || (qm + 32 > L);
-        bf16x8 pa[2], da[2];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int qi = 32 * mq + 8 * (i >> 2) + 4 * h + (i & 3);
-          float pr = fast_exp2(s[i] * p.scale_log2 - lse_s[qi]);
-          if (need_mask) {
-            const int32_t qa = qs + qi;
-            if (qa < key || qa >= L) pr = 0.f;
-          }
-          const float ds = pr * (dp[i] - D_s[qi]);
-          pa[i >> 3][i & 7] = (bf16)pr;
-          da[i >> 3][i & 7] = (bf16)ds;
-        }
-#pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt) {
-          const int col = 32 * dt + dsub + 4 * (gi & 3);
-#pragma unroll
-          for (int ks = 0; ks < 2; ++ks) {
-            const int row = 32 * mq + 16 * ks + 4 * h + (gi >> 2);
-            const bf16* po = &dOs[row * S + col];
-            const bf16* pq = &Qs[row * S + col];
-            const bf16x8 bo = tr_read8(po, po + 8 * S);
-            const bf16x8 bq = tr_read8(pq, pq + 8 * S);
-            dva[dt] = mfma32(pa[ks], bo, dva[dt]);
-            dka[dt] = mfma32(da[ks], bq, dka[dt]);
-          }
-        }
-      }
+  for (int32_t t = 0; t < niter; t += 2) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (t + 1 < niter) issue(t + 1, Qs1, dOs1, l2s1, Ds1);
+    {
+      const int32_t qs = kb + (t % nqb) * kBMk;
+      if (qs + kBMk - 1 >= wk_lo) dkdv_block<D>(st, Qs0, dOs0, l2s0, Ds0, qs, L, key, wk_lo, c2, h, lq, l);
+    }
+    if (t + 1 >= niter) break;
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (t + 2 < niter) issue(t + 2, Qs0, dOs0, l2s0, Ds0);
+    {
+      const int32_t qs = kb + ((t + 1) % nqb) * kBMk;
+      if (qs + kBMk - 1 >= wk_lo) dkdv_block<D>(st, Qs1, dOs1, l2s1, Ds1, qs, L, key, wk_lo, c2, h, lq, l);
     }
   }
 
-  // dka/dva C layout: key = kb + 32*w + 8*(i/4) + 4*h + i%4, d = 32*dt + lq
+  // dka/dva C layout: key = wk_lo + 8*(i/4) + 4*h + i%4, d = 32*dt + lq
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     const int32_t kr = wk_lo + 8 * (i >> 2) + 4 * h + (i & 3);
@@ -319,8 +375,8 @@ __global__ void __launch_bounds__(kThreads, 1) k_bwd_dkdv(BwdParams p) {
       float* dvr = p.dv + ((int64_t)(s0 + kr) * p.hkv + kvh) * D;
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) {
-        dkr[32 * dt + lq] = dka[dt][i] * p.scale;
-        dvr[32 * dt + lq] = dva[dt][i];
+        dkr[32 * dt + lq] = st.dka[dt][i] * p.scale;
+        dvr[32 * dt + lq] = st.dva[dt][i];
       }
     }
   }
@@ -328,11 +384,11 @@ __global__ void __launch_bounds__(kThreads, 1) k_bwd_dkdv(BwdParams p) {
 
 }  // namespace
 
-static size_t dbuf_bytes(const AttnDims& d) { return align_up(sizeof(float) * (size_t)d.hq * d.T, 256); }
+static size_t vec_bytes(const AttnDims& d) { return align_up(sizeof(float) * (size_t)d.hq * d.T, 256); }
 
 size_t attn_bwd_workspace_bytes(int dtype, const AttnDims& d) {
-  if (dtype != 1) return dbuf_bytes(d);
-  return dbuf_bytes(d) + schedule_bytes(d.T, d.n_seg, d.max_seqlen, kBQ, kBNq) +
+  if (dtype != 1) return vec_bytes(d);
+  return 2 * vec_bytes(d) + schedule_bytes(d.T, d.n_seg, d.max_seqlen, kBQ, kBNq) +
          schedule_bytes(d.T, d.n_seg, d.max_seqlen, kBKV, kBMk);
 }
 
@@ -340,7 +396,9 @@ hipError_t launch_attn_bwd_bf16(const AttnBwdArgs& a, hipStream_t stream) {
   const AttnDims& d = a.dims;
   char* ws = static_cast<char*>(a.workspace);
   float* Dbuf = reinterpret_cast<float*>(ws);
-  ws += dbuf_bytes(d);
+  ws += vec_bytes(d);
+  float* L2buf = reinterpret_cast<float*>(ws);
+  ws += vec_bytes(d);
   TileSchedule sq = schedule_carve(ws, d.T, d.n_seg, d.max_seqlen, kBQ, kBNq);
   ws += schedule_bytes(d.T, d.n_seg, d.max_seqlen, kBQ, kBNq);
   TileSchedule sk = schedule_carve(ws, d.T, d.n_seg, d.max_seqlen, kBKV, kBMk);
@@ -353,6 +411,7 @@ hipError_t launch_attn_bwd_bf16(const AttnBwdArgs& a, hipStream_t stream) {
   p.dout = static_cast<const bf16*>(a.dout);
   p.lse = a.lse;
   p.Dbuf = Dbuf;
+  p.L2buf = L2buf;
   p.dq = a.dq;
   p.dk = a.dk;
   p.dv = a.dv;
@@ -370,14 +429,13 @@ hipError_t launch_attn_bwd_bf16(const AttnBwdArgs& a, hipStream_t stream) {
   p.scale_log2 = d.scale * kLog2e;
   if (d.T == 0) return hipSuccess;
 
-  const int64_t pre_threads = d.T * d.hq * (d.d / 8);
-  const unsigned pre_grid = (unsigned)((pre_threads + kThreads - 1) / kThreads);
   {
     ScopedKernelTimer timed(kTimeBwdPre, stream);
+    dim3 grid((unsigned)((d.T + 63) / 64), (unsigned)d.hq);
     if (d.d == 128)
-      k_bwd_pre<128><<<pre_grid, kThreads, 0, stream>>>(p);
+      k_bwd_pre<128><<<grid, kThreads, 0, stream>>>(p);
     else
-      k_bwd_pre<64><<<pre_grid, kThreads, 0, stream>>>(p);
+      k_bwd_pre<64><<<grid, kThreads, 0, stream>>>(p);
   }
 
   hipError_t e = launch_schedule(a.cu, d.n_seg, (int32_t)d.T, kBKV, kBMk, true, sk, stream);

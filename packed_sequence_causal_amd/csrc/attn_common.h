@@ -73,6 +73,57 @@ __device__ __forceinline__ uint32_t xcd_group_remap(uint32_t b, uint32_t n, uint
   return c * win + (r % 8u) * g + r / 8u;
 }
 
+// ------------------------------------------------------------------ LDS tiles
+//
+// A tile of ROWS rows x D bf16 columns lives in LDS without padding, as 16-byte
+// chunks; chunk c of row r sits in slot c ^ swz(r) of that row.  The swizzle
+// keeps the two read patterns the kernels use free of bank conflicts: 16 lanes
+// reading chunk c of 16 consecutive rows (MFMA operand rows, ds_read_b128),
+// and ds_read_b64_tr_b16 groups reading 8-byte pieces of chunks c, c+1 (c
+// even) of 4 consecutive rows starting at a multiple of 4.
+template <int D>
+__device__ __forceinline__ int lds_slot(int r, int c) {
+  if constexpr (D == 128) return c ^ (((r & 7) << 1) | ((r >> 3) & 1));
+  else return c ^ (((r & 3) << 1) | ((r >> 2) & 1));
+}
+// Byte offset of element e (a multiple of 4) of row r.
+template <int D>
+__device__ __forceinline__ int lds_byte(int r, int e) {
+  return (r * (D / 8) + lds_slot<D>(r, e >> 3)) * 16 + (e & 7) * 2;
+}
+
+// Asynchronous load of rows [row0, row0 + ROWS) of a [T, heads, D] operand
+// (base already points at the segment start and head) into one LDS tile,
+// spread over NW waves (w = this wave).  global_load_lds_dwordx4 writes 64
+// consecutive 16-byte slots in lane order, so each lane fetches the global
+// chunk that belongs at its slot (the swizzle is an involution).  Rows at or
+// past `L` repeat row L - 1: their scores are masked, any finite data will do.
+// Completion is tracked by vmcnt; wait, then barrier, before reading the tile.
+template <int D, int ROWS, int NW>
+__device__ __forceinline__ void load_tile_async(const bf16* base, int64_t stride, int32_t row0, int32_t L,
+                                                void* lds, int w, int l) {
+  constexpr int CPR = D / 8;
+  constexpr int LOADS = ROWS * CPR / 64;
+  static_assert(LOADS % NW == 0, "tile loads must split evenly over the waves");
+#pragma unroll
+  for (int i = 0; i < LOADS / NW; ++i) {
+    const int t = w + NW * i;
+    const int slot = 64 * t + l;
+    const int r = slot / CPR;
+    const int c = lds_slot<D>(r, slot % CPR);
+    const int32_t row = min(row0 + r, L - 1);
+    __builtin_amdgcn_global_load_lds(base + (int64_t)row * stride + c * 8,
+                                     (PSC_LDS void*)(static_cast<char*>(lds) + 64 * t * 16), 16, 0, 0);
+  }
+}
+
+// Asynchronous load of 64 consecutive floats vec[row0 .. row0 + 64) (rows at or
+// past L repeat row L - 1) into LDS, one 4-byte slot per lane of one wave.
+__device__ __forceinline__ void load_vec64_async(const float* vec, int32_t row0, int32_t L, void* lds, int l) {
+  const int32_t row = min(row0 + l, L - 1);
+  __builtin_amdgcn_global_load_lds(vec + row, (PSC_LDS void*)lds, 4, 0, 0);
+}
+
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 

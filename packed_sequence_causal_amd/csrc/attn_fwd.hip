@@ -47,46 +47,12 @@ struct FwdParams {
   float scale_log2;
 };
 
-template <int D>
-struct Tile {
-  static constexpr int CPR = D / 8;          // 16-byte chunks per row
-  static constexpr int CHUNKS = kBN * CPR;   // chunks per K (or V) tile
-  static constexpr int LOADS = CHUNKS / 64;  // wave-wide load instructions per tile
-  static constexpr int LOADS_PER_WAVE = LOADS / (kThreads / 64);
-  static constexpr int BYTES = CHUNKS * 16;
-};
-
-// Slot of logical 16-byte chunk c of row r inside the row (XOR swizzle).
-template <int D>
-__device__ __forceinline__ int lds_slot(int r, int c) {
-  if constexpr (D == 128) return c ^ (((r & 7) << 1) | ((r >> 3) & 1));
-  else return c ^ (((r & 3) << 1) | ((r >> 2) & 1));
-}
-// Byte offset of element e (a multiple of 4) of row r.
-template <int D>
-__device__ __forceinline__ int lds_byte(int r, int e) {
-  return (r * Tile<D>::CPR + lds_slot<D>(r, e >> 3)) * 16 + (e & 7) * 2;
-}
-
-// Issue the asynchronous loads of key/value rows [kb, kb + 64) of the segment
-// into one LDS stage.  Rows past the segment end repeat its last row (their
-// scores are masked, so any finite data will do).
+// Asynchronous loads of key/value rows [kb, kb + 64) into one LDS stage.
 template <int D>
 __device__ __forceinline__ void load_kv(const bf16* Kp, const bf16* Vp, int64_t sk, int64_t sv, int32_t kb,
                                         int32_t L, bf16* Ks, bf16* Vs, int w, int l) {
-  using T_ = Tile<D>;
-#pragma unroll
-  for (int i = 0; i < T_::LOADS_PER_WAVE; ++i) {
-    const int t = w + 4 * i;          // load instruction index within the tile
-    const int slot = 64 * t + l;      // physical chunk this lane writes
-    const int r = slot / T_::CPR;
-    const int c = lds_slot<D>(r, slot % T_::CPR);  // the swizzle is an involution
-    const int32_t key = min(kb + r, L - 1);
-    __builtin_amdgcn_global_load_lds(Kp + (int64_t)key * sk + c * 8,
-                                     (PSC_LDS void*)(reinterpret_cast<char*>(Ks) + 64 * t * 16), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(Vp + (int64_t)key * sv + c * 8,
-                                     (PSC_LDS void*)(reinterpret_cast<char*>(Vs) + 64 * t * 16), 16, 0, 0);
-  }
+  load_tile_async<D, kBN, kThreads / 64>(Kp, sk, kb, L, Ks, w, l);
+  load_tile_async<D, kBN, kThreads / 64>(Vp, sv, kb, L, Vs, w, l);
 }
 
 template <int D>
@@ -168,11 +134,10 @@ __device__ __forceinline__ void fwd_block(FwdState<D>& st, const bf16* Ks, const
 
 template <int D>
 __global__ void __launch_bounds__(kThreads, 2) k_attn_fwd(FwdParams p) {
-  using T_ = Tile<D>;
-  __shared__ __attribute__((aligned(16))) bf16 Ks0[T_::BYTES / 2];
-  __shared__ __attribute__((aligned(16))) bf16 Vs0[T_::BYTES / 2];
-  __shared__ __attribute__((aligned(16))) bf16 Ks1[T_::BYTES / 2];
-  __shared__ __attribute__((aligned(16))) bf16 Vs1[T_::BYTES / 2];
+  __shared__ __attribute__((aligned(16))) bf16 Ks0[kBN * D];
+  __shared__ __attribute__((aligned(16))) bf16 Vs0[kBN * D];
+  __shared__ __attribute__((aligned(16))) bf16 Ks1[kBN * D];
+  __shared__ __attribute__((aligned(16))) bf16 Vs1[kBN * D];
 
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, h = l >> 5, lq = l & 31;
   const uint32_t b = xcd_group_remap(blockIdx.x, gridDim.x, (uint32_t)p.group);
