@@ -95,7 +95,7 @@ struct DqState {
 
 // One 64-key block of the dQ loop for one wave.
 template <int D>
-__device__ __forceinline__ void dq_block(DqState<D>& st, const bf16* Ks, const bf16* Vs, int32_t kb, int32_t L,
+__device__ __forceinline__ void dq_block(DqState<D>& st, const char* Ks, const char* Vs, int32_t kb, int32_t L,
                                          int32_t qrow, int32_t wq_lo, float c2, int h, int lq, int l) {
   const char* Kb = reinterpret_cast<const char*>(Ks);
   const char* Vb = reinterpret_cast<const char*>(Vs);
@@ -107,8 +107,8 @@ __device__ __forceinline__ void dq_block(DqState<D>& st, const bf16* Ks, const b
     const int r = 32 * n2 + lq;
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) {
-      const bf16x8 ak = *reinterpret_cast<const bf16x8*>(Kb + lds_byte<D>(r, 16 * kk + 8 * h));
-      const bf16x8 av = *reinterpret_cast<const bf16x8*>(Vb + lds_byte<D>(r, 16 * kk + 8 * h));
+      const bf16x8 ak = *reinterpret_cast<const bf16x8*>(Kb + lds_byte(r, 16 * kk + 8 * h));
+      const bf16x8 av = *reinterpret_cast<const bf16x8*>(Vb + lds_byte(r, 16 * kk + 8 * h));
       s[n2] = mfma32(ak, st.qf[kk], s[n2]);
       dp[n2] = mfma32(av, st.df[kk], dp[n2]);
     }
@@ -141,8 +141,8 @@ __device__ __forceinline__ void dq_block(DqState<D>& st, const bf16* Ks, const b
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       const int r0 = 16 * ks + 4 * h + (gi >> 2);
-      const bf16* p0 = reinterpret_cast<const bf16*>(Kb + lds_byte<D>(r0, col));
-      const bf16* p1 = reinterpret_cast<const bf16*>(Kb + lds_byte<D>(r0 + 8, col));
+      const bf16* p0 = reinterpret_cast<const bf16*>(Kb + lds_byte(r0, col));
+      const bf16* p1 = reinterpret_cast<const bf16*>(Kb + lds_byte(r0 + 8, col));
       st.acc[dt] = mfma32(tr_read8(p0, p1), dsb[ks], st.acc[dt]);
     }
   }
@@ -150,10 +150,10 @@ __device__ __forceinline__ void dq_block(DqState<D>& st, const bf16* Ks, const b
 
 template <int D>
 __global__ void __launch_bounds__(kThreads, 2) k_bwd_dq(BwdParams p) {
-  __shared__ __attribute__((aligned(16))) bf16 Ks0[kBNq * D];
-  __shared__ __attribute__((aligned(16))) bf16 Vs0[kBNq * D];
-  __shared__ __attribute__((aligned(16))) bf16 Ks1[kBNq * D];
-  __shared__ __attribute__((aligned(16))) bf16 Vs1[kBNq * D];
+  __shared__ __attribute__((aligned(16))) char Ks0[tile_bytes<D>()];
+  __shared__ __attribute__((aligned(16))) char Vs0[tile_bytes<D>()];
+  __shared__ __attribute__((aligned(16))) char Ks1[tile_bytes<D>()];
+  __shared__ __attribute__((aligned(16))) char Vs1[tile_bytes<D>()];
 
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, h = l >> 5, lq = l & 31;
   const uint32_t b = xcd_group_remap(blockIdx.x, gridDim.x, (uint32_t)p.group);
@@ -170,8 +170,8 @@ __global__ void __launch_bounds__(kThreads, 2) k_bwd_dq(BwdParams p) {
   const bf16* Vp = p.v + (int64_t)s0 * p.sv + (int64_t)kvh * D;
   const int32_t kv_end = min(q0 + kBQ, L);
   const int32_t nkv = (kv_end + kBNq - 1) / kBNq;
-  load_tile_async<D, kBNq, kThreads / 64>(Kp, p.sk, 0, L, Ks0, w, l);
-  load_tile_async<D, kBNq, kThreads / 64>(Vp, p.sv, 0, L, Vs0, w, l);
+  load_tile_async<D, kThreads / 64>(Kp, p.sk, 0, L, Ks0, w, l);
+  load_tile_async<D, kThreads / 64>(Vp, p.sv, 0, L, Vs0, w, l);
 
   const int32_t qrow = q0 + 32 * w + lq;
   const bool qvalid = qrow < L;
@@ -196,16 +196,16 @@ __global__ void __launch_bounds__(kThreads, 2) k_bwd_dq(BwdParams p) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (j + 1 < nkv) {
-      load_tile_async<D, kBNq, kThreads / 64>(Kp, p.sk, (j + 1) * kBNq, L, Ks1, w, l);
-      load_tile_async<D, kBNq, kThreads / 64>(Vp, p.sv, (j + 1) * kBNq, L, Vs1, w, l);
+      load_tile_async<D, kThreads / 64>(Kp, p.sk, (j + 1) * kBNq, L, Ks1, w, l);
+      load_tile_async<D, kThreads / 64>(Vp, p.sv, (j + 1) * kBNq, L, Vs1, w, l);
     }
     if (j * kBNq <= wq_hi) dq_block<D>(st, Ks0, Vs0, j * kBNq, L, qrow, wq_lo, c2, h, lq, l);
     if (j + 1 >= nkv) break;
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (j + 2 < nkv) {
-      load_tile_async<D, kBNq, kThreads / 64>(Kp, p.sk, (j + 2) * kBNq, L, Ks0, w, l);
-      load_tile_async<D, kBNq, kThreads / 64>(Vp, p.sv, (j + 2) * kBNq, L, Vs0, w, l);
+      load_tile_async<D, kThreads / 64>(Kp, p.sk, (j + 2) * kBNq, L, Ks0, w, l);
+      load_tile_async<D, kThreads / 64>(Vp, p.sv, (j + 2) * kBNq, L, Vs0, w, l);
     }
     if ((j + 1) * kBNq <= wq_hi) dq_block<D>(st, Ks1, Vs1, (j + 1) * kBNq, L, qrow, wq_lo, c2, h, lq, l);
   }
@@ -236,7 +236,7 @@ struct DkvState {
 // One 64-query block of the dK/dV loop for one wave (keys wk_lo .. wk_lo+31,
 // this lane's key `key`).
 template <int D>
-__device__ __forceinline__ void dkdv_block(DkvState<D>& st, const bf16* Qs, const bf16* dOs, const float* l2s,
+__device__ __forceinline__ void dkdv_block(DkvState<D>& st, const char* Qs, const char* dOs, const float* l2s,
                                            const float* Ds, int32_t qs, int32_t L, int32_t key, int32_t wk_lo,
                                            float c2, int h, int lq, int l) {
   const char* Qb = reinterpret_cast<const char*>(Qs);
@@ -251,8 +251,8 @@ __device__ __forceinline__ void dkdv_block(DkvState<D>& st, const bf16* Qs, cons
     const int r = 32 * mq + lq;
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) {
-      const bf16x8 aq = *reinterpret_cast<const bf16x8*>(Qb + lds_byte<D>(r, 16 * kk + 8 * h));
-      const bf16x8 ad = *reinterpret_cast<const bf16x8*>(Ob + lds_byte<D>(r, 16 * kk + 8 * h));
+      const bf16x8 aq = *reinterpret_cast<const bf16x8*>(Qb + lds_byte(r, 16 * kk + 8 * h));
+      const bf16x8 ad = *reinterpret_cast<const bf16x8*>(Ob + lds_byte(r, 16 * kk + 8 * h));
       s = mfma32(aq, st.kf[kk], s);
       dp = mfma32(ad, st.vf[kk], dp);
     }
@@ -283,10 +283,10 @@ __device__ __forceinline__ void dkdv_block(DkvState<D>& st, const bf16* Qs, cons
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         const int r0 = 32 * mq + 16 * ks + 4 * h + (gi >> 2);
-        const bf16x8 bo = tr_read8(reinterpret_cast<const bf16*>(Ob + lds_byte<D>(r0, col)),
-                                   reinterpret_cast<const bf16*>(Ob + lds_byte<D>(r0 + 8, col)));
-        const bf16x8 bq = tr_read8(reinterpret_cast<const bf16*>(Qb + lds_byte<D>(r0, col)),
-                                   reinterpret_cast<const bf16*>(Qb + lds_byte<D>(r0 + 8, col)));
+        const bf16x8 bo = tr_read8(reinterpret_cast<const bf16*>(Ob + lds_byte(r0, col)),
+                                   reinterpret_cast<const bf16*>(Ob + lds_byte(r0 + 8, col)));
+        const bf16x8 bq = tr_read8(reinterpret_cast<const bf16*>(Qb + lds_byte(r0, col)),
+                                   reinterpret_cast<const bf16*>(Qb + lds_byte(r0 + 8, col)));
         st.dva[dt] = mfma32(pa[ks], bo, st.dva[dt]);
         st.dka[dt] = mfma32(da[ks], bq, st.dka[dt]);
       }
@@ -296,10 +296,10 @@ __device__ __forceinline__ void dkdv_block(DkvState<D>& st, const bf16* Qs, cons
 
 template <int D>
 __global__ void __launch_bounds__(kThreads, 1) k_bwd_dkdv(BwdParams p) {
-  __shared__ __attribute__((aligned(16))) bf16 Qs0[kBMk * D];
-  __shared__ __attribute__((aligned(16))) bf16 dOs0[kBMk * D];
-  __shared__ __attribute__((aligned(16))) bf16 Qs1[kBMk * D];
-  __shared__ __attribute__((aligned(16))) bf16 dOs1[kBMk * D];
+  __shared__ __attribute__((aligned(16))) char Qs0[tile_bytes<D>()];
+  __shared__ __attribute__((aligned(16))) char dOs0[tile_bytes<D>()];
+  __shared__ __attribute__((aligned(16))) char Qs1[tile_bytes<D>()];
+  __shared__ __attribute__((aligned(16))) char dOs1[tile_bytes<D>()];
   __shared__ __attribute__((aligned(16))) float l2s0[kBMk];
   __shared__ __attribute__((aligned(16))) float Ds0[kBMk];
   __shared__ __attribute__((aligned(16))) float l2s1[kBMk];
@@ -320,11 +320,11 @@ __global__ void __launch_bounds__(kThreads, 1) k_bwd_dkdv(BwdParams p) {
   const int32_t niter = p.group * nqb;
 
   // iteration t: query head kvh*G + t / nqb, query block kb + (t % nqb) * 64
-  auto issue = [&](int32_t t, bf16* Qs, bf16* dOs, float* l2s, float* Ds) {
+  auto issue = [&](int32_t t, char* Qs, char* dOs, float* l2s, float* Ds) {
     const int32_t head = kvh * p.group + t / nqb;
     const int32_t qs = kb + (t % nqb) * kBMk;
-    load_tile_async<D, kBMk, kThreads / 64>(p.q + (int64_t)s0 * p.sq + (int64_t)head * D, p.sq, qs, L, Qs, w, l);
-    load_tile_async<D, kBMk, kThreads / 64>(p.dout + (int64_t)s0 * p.sdo + (int64_t)head * D, p.sdo, qs, L, dOs,
+    load_tile_async<D, kThreads / 64>(p.q + (int64_t)s0 * p.sq + (int64_t)head * D, p.sq, qs, L, Qs, w, l);
+    load_tile_async<D, kThreads / 64>(p.dout + (int64_t)s0 * p.sdo + (int64_t)head * D, p.sdo, qs, L, dOs,
                                            w, l);
     if (w == 0) load_vec64_async(p.L2buf + (int64_t)head * p.T + s0, qs, L, l2s, l);
     if (w == 1) load_vec64_async(p.Dbuf + (int64_t)head * p.T + s0, qs, L, Ds, l);

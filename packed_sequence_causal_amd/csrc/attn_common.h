@@ -73,47 +73,79 @@ __device__ __forceinline__ uint32_t xcd_group_remap(uint32_t b, uint32_t n, uint
   return c * win + (r % 8u) * g + r / 8u;
 }
 
-// ------------------------------------------------------------------ LDS tiles
-//
-// A tile of ROWS rows x D bf16 columns lives in LDS without padding, as 16-byte
-// chunks; chunk c of row r sits in slot c ^ swz(r) of that row.  The swizzle
-// keeps the two read patterns the kernels use free of bank conflicts: 16 lanes
-// reading chunk c of 16 consecutive rows (MFMA operand rows, ds_read_b128),
-// and ds_read_b64_tr_b16 groups reading 8-byte pieces of chunks c, c+1 (c
-// even) of 4 consecutive rows starting at a multiple of 4.
-template <int D>
-__device__ __forceinline__ int lds_slot(int r, int c) {
-  if constexpr (D == 128) return c ^ (((r & 7) << 1) | ((r >> 3) & 1));
-  else return c ^ (((r & 3) << 1) | ((r >> 2) & 1));
+// Asynchronous global -> LDS copy of 16 (or 4) bytes per lane:
+// global_load_lds_dwordx4 writes lane i's data to LDS byte M0 + 16*i.  Issued
+// through inline assembly so the compiler's wait-count bookkeeping does not
+// see it: once such a copy is in flight LLVM can only wait for *all*
+// outstanding LDS reads (lgkmcnt(0)) instead of the ones an MFMA needs.
+// Completion is the caller's job: s_waitcnt vmcnt(0) then a barrier before
+// the destination is read, and no read of a destination while it is written.
+// `lds` must be wave-uniform.
+__device__ __forceinline__ void lds_dma16(const void* src, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(src) : "memory", "m0");
 }
-// Byte offset of element e (a multiple of 4) of row r.
-template <int D>
-__device__ __forceinline__ int lds_byte(int r, int e) {
-  return (r * (D / 8) + lds_slot<D>(r, e >> 3)) * 16 + (e & 7) * 2;
+__device__ __forceinline__ void lds_dma4(const void* src, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" ::"s"(lds), "v"(src) : "memory", "m0");
+}
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)((PSC_LDS const char*)p);
 }
 
-// Asynchronous load of rows [row0, row0 + ROWS) of a [T, heads, D] operand
-// (base already points at the segment start and head) into one LDS tile,
-// spread over NW waves (w = this wave).  global_load_lds_dwordx4 writes 64
-// consecutive 16-byte slots in lane order, so each lane fetches the global
-// chunk that belongs at its slot (the swizzle is an involution).  Rows at or
-// past `L` repeat row L - 1: their scores are masked, any finite data will do.
-// Completion is tracked by vmcnt; wait, then barrier, before reading the tile.
-template <int D, int ROWS, int NW>
+// ------------------------------------------------------------------ LDS tiles
+//
+// A tile of 64 rows x D bf16 columns is stored as D/64 column groups of eight
+// 16-byte chunks (128 bytes of each row); inside a group the rows are 128
+// bytes apart and chunk j of row r sits in slot j ^ swz(r).  swz was chosen
+// (checked exhaustively for 64 four-byte banks) so that both read patterns of
+// the kernels are free of bank conflicts:
+//   * MFMA operand rows (ds_read_b128): 16 lanes read chunk c of 16
+//     consecutive rows;
+//   * column reads (ds_read_b64_tr_b16): a 16-lane group reads 8-byte halves
+//     of chunks c and c+1 (c even) of 4 consecutive rows starting at a
+//     multiple of 4;
+// and, since swz(r) depends only on bits 1..3 of r, a lane needs just a few
+// precomputed offsets for all its reads.  One asynchronous load instruction
+// fills 8 rows of one group: 8 contiguous 128-byte row pieces from global
+// memory.
+constexpr int kTileRows = 64;
+constexpr int kGroupBytes = kTileRows * 128;
+template <int D>
+constexpr int tile_bytes() { return (D / 64) * kGroupBytes; }
+
+__device__ __forceinline__ int lds_swz(int r) { return (((r >> 1) & 1) << 2) | ((r >> 2) & 3); }
+
+// Byte offset of element e (a multiple of 4) of row r.
+__device__ __forceinline__ int lds_byte(int r, int e) {
+  const int c = e >> 3;
+  return (c >> 3) * kGroupBytes + r * 128 + (((c & 7) ^ lds_swz(r)) << 4) + (e & 7) * 2;
+}
+
+// Asynchronous load of rows [row0, row0 + 64) of a [T, heads, D] operand (base
+// already points at the segment start and head) into one LDS tile, spread
+// over NW waves (w = this wave).  global_load_lds_dwordx4 writes the 64 lanes'
+// 16 bytes to 64 consecutive LDS slots; instruction t covers rows
+// 8*(t%8) .. +7 of column group t/8, and each lane fetches the chunk that the
+// swizzle places at its slot.  Rows at or past `L` repeat row L - 1: their
+// scores are masked, any finite data will do.  Completion is tracked by
+// vmcnt; wait, then barrier, before reading the tile.
+template <int D, int NW>
 __device__ __forceinline__ void load_tile_async(const bf16* base, int64_t stride, int32_t row0, int32_t L,
                                                 void* lds, int w, int l) {
-  constexpr int CPR = D / 8;
-  constexpr int LOADS = ROWS * CPR / 64;
+  constexpr int LOADS = D / 8;  // 64 rows x D/8 chunks / 64 lanes
   static_assert(LOADS % NW == 0, "tile loads must split evenly over the waves");
+  const int rr = l >> 3;   // row inside the 8-row piece
+  const int p = l & 7;     // slot inside the row
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  const uint32_t lds0 = lds_addr(lds);
 #pragma unroll
   for (int i = 0; i < LOADS / NW; ++i) {
     const int t = w + NW * i;
-    const int slot = 64 * t + l;
-    const int r = slot / CPR;
-    const int c = lds_slot<D>(r, slot % CPR);
-    const int32_t row = min(row0 + r, L - 1);
-    __builtin_amdgcn_global_load_lds(base + (int64_t)row * stride + c * 8,
-                                     (PSC_LDS void*)(static_cast<char*>(lds) + 64 * t * 16), 16, 0, 0);
+    const int tu = wu + NW * i;
+    const int g = t >> 3;
+    const int r = 8 * (t & 7) + rr;
+    const int c = 8 * g + (p ^ lds_swz(r));
+    const bf16* src = base + (int64_t)min(row0 + r, L - 1) * stride + c * 8;
+    lds_dma16(src, lds0 + (tu >> 3) * kGroupBytes + (tu & 7) * 1024);
   }
 }
 
@@ -121,7 +153,40 @@ __device__ __forceinline__ void load_tile_async(const bf16* base, int64_t stride
 // past L repeat row L - 1) into LDS, one 4-byte slot per lane of one wave.
 __device__ __forceinline__ void load_vec64_async(const float* vec, int32_t row0, int32_t L, void* lds, int l) {
   const int32_t row = min(row0 + l, L - 1);
-  __builtin_amdgcn_global_load_lds(vec + row, (PSC_LDS void*)lds, 4, 0, 0);
+  lds_dma4(vec + row, lds_addr(lds));
+}
+
+// Scheduling hints: keep `n` LDS reads / MFMAs / VALU ops together, in the
+// order the calls appear (llvm.amdgcn.sched.group.barrier masks).
+#define PSC_SCHED_DS_READ(n) __builtin_amdgcn_sched_group_barrier(0x0100, (n), 0)
+#define PSC_SCHED_MFMA(n) __builtin_amdgcn_sched_group_barrier(0x0008, (n), 0)
+#define PSC_SCHED_VALU(n) __builtin_amdgcn_sched_group_barrier(0x0002, (n), 0)
+
+// acc[n] += A_n B over k = 0..KS-1 for two row blocks n = 0, 1 whose A
+// fragments are 16-byte LDS reads at a0 + off(kk) and a1 + off(kk), with one
+// k-step of read-ahead so every MFMA finds its operands already loaded.
+template <int KS, typename Off>
+__device__ __forceinline__ void mfma_rows2(f32x16& acc0, f32x16& acc1, const char* a0, const char* a1,
+                                           const bf16x8* b, Off off) {
+  bf16x8 x0 = *reinterpret_cast<const bf16x8*>(a0 + off(0));
+  bf16x8 x1 = *reinterpret_cast<const bf16x8*>(a1 + off(0));
+#pragma unroll
+  for (int kk = 0; kk < KS; ++kk) {
+    bf16x8 y0 = x0, y1 = x1;
+    if (kk + 1 < KS) {
+      x0 = *reinterpret_cast<const bf16x8*>(a0 + off(kk + 1));
+      x1 = *reinterpret_cast<const bf16x8*>(a1 + off(kk + 1));
+    }
+    acc0 = mfma32(y0, b[kk], acc0);
+    acc1 = mfma32(y1, b[kk], acc1);
+  }
+  PSC_SCHED_DS_READ(2);
+#pragma unroll
+  for (int kk = 0; kk + 1 < KS; ++kk) {
+    PSC_SCHED_DS_READ(2);
+    PSC_SCHED_MFMA(2);
+  }
+  PSC_SCHED_MFMA(2);
 }
 
 constexpr float kLog2e = 1.4426950408889634f;

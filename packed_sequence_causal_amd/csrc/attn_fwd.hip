@@ -50,9 +50,9 @@ struct FwdParams {
 // Asynchronous loads of key/value rows [kb, kb + 64) into one LDS stage.
 template <int D>
 __device__ __forceinline__ void load_kv(const bf16* Kp, const bf16* Vp, int64_t sk, int64_t sv, int32_t kb,
-                                        int32_t L, bf16* Ks, bf16* Vs, int w, int l) {
-  load_tile_async<D, kBN, kThreads / 64>(Kp, sk, kb, L, Ks, w, l);
-  load_tile_async<D, kBN, kThreads / 64>(Vp, sv, kb, L, Vs, w, l);
+                                        int32_t L, char* Ks, char* Vs, int w, int l) {
+  load_tile_async<D, kThreads / 64>(Kp, sk, kb, L, Ks, w, l);
+  load_tile_async<D, kThreads / 64>(Vp, sv, kb, L, Vs, w, l);
 }
 
 template <int D>
@@ -64,21 +64,13 @@ struct FwdState {
 
 // One 64-key block for one wave.
 template <int D>
-__device__ __forceinline__ void fwd_block(FwdState<D>& st, const bf16* Ks, const bf16* Vs, int32_t kb, int32_t L,
+__device__ __forceinline__ void fwd_block(FwdState<D>& st, const char* Ks, const char* Vs, int32_t kb, int32_t L,
                                           int32_t qrow, int32_t wq_lo, float c2, int h, int lq, int l) {
   const char* Kb = reinterpret_cast<const char*>(Ks);
   const char* Vb = reinterpret_cast<const char*>(Vs);
-  f32x16 s[2];
-#pragma unroll
-  for (int n2 = 0; n2 < 2; ++n2) {
-    s[n2] = f32x16{};
-    const int r = 32 * n2 + lq;
-#pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(Kb + lds_byte<D>(r, 16 * kk + 8 * h));
-      s[n2] = mfma32(a, st.qf[kk], s[n2]);
-    }
-  }
+  f32x16 s[2] = {f32x16{}, f32x16{}};
+  // rows lq and 32 + lq share the swizzle (it depends on row bits 1..3 only)
+  mfma_rows2<D / 16>(s[0], s[1], Kb, Kb + 32 * 128, st.qf, [&](int kk) { return lds_byte(lq, 16 * kk + 8 * h); });
   if ((kb + kBN - 1 > wq_lo) || (kb + kBN > L)) {
 #pragma unroll
     for (int n2 = 0; n2 < 2; ++n2) {
@@ -125,8 +117,8 @@ __device__ __forceinline__ void fwd_block(FwdState<D>& st, const bf16* Ks, const
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       const int r0 = 16 * ks + 4 * h + (gi >> 2);
-      const bf16* p0 = reinterpret_cast<const bf16*>(Vb + lds_byte<D>(r0, col));
-      const bf16* p1 = reinterpret_cast<const bf16*>(Vb + lds_byte<D>(r0 + 8, col));
+      const bf16* p0 = reinterpret_cast<const bf16*>(Vb + lds_byte(r0, col));
+      const bf16* p1 = reinterpret_cast<const bf16*>(Vb + lds_byte(r0 + 8, col));
       st.oacc[dt] = mfma32(tr_read8(p0, p1), pb[ks], st.oacc[dt]);
     }
   }
@@ -134,10 +126,10 @@ __device__ __forceinline__ void fwd_block(FwdState<D>& st, const bf16* Ks, const
 
 template <int D>
 __global__ void __launch_bounds__(kThreads, 2) k_attn_fwd(FwdParams p) {
-  __shared__ __attribute__((aligned(16))) bf16 Ks0[kBN * D];
-  __shared__ __attribute__((aligned(16))) bf16 Vs0[kBN * D];
-  __shared__ __attribute__((aligned(16))) bf16 Ks1[kBN * D];
-  __shared__ __attribute__((aligned(16))) bf16 Vs1[kBN * D];
+  __shared__ __attribute__((aligned(16))) char Ks0[tile_bytes<D>()];
+  __shared__ __attribute__((aligned(16))) char Vs0[tile_bytes<D>()];
+  __shared__ __attribute__((aligned(16))) char Ks1[tile_bytes<D>()];
+  __shared__ __attribute__((aligned(16))) char Vs1[tile_bytes<D>()];
 
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, h = l >> 5, lq = l & 31;
   const uint32_t b = xcd_group_remap(blockIdx.x, gridDim.x, (uint32_t)p.group);
