@@ -11,9 +11,11 @@
 // into one causal problem per document).
 //
 // Tiles are ordered by decreasing work (longest processing time first) with a
-// counting sort over work measured in `unit`-row blocks: histogram, descending
-// exclusive scan, scatter.  Ties are placed in atomic order; each tile's result
-// does not depend on the order.
+// counting sort over work measured in `unit`-row blocks.  Every stage is
+// parallel over tiles: per-segment tile counts and their scan (one block), a
+// histogram of tile bins, a descending scan of the bins, and a scatter in
+// which each tile takes the next slot of its bin.  Ties are placed in atomic
+// order; each tile's result does not depend on the order.
 #include "psc_internal.h"
 
 namespace psc {
@@ -25,31 +27,77 @@ __device__ inline int32_t tile_work(int32_t L, int32_t t, int32_t tile, bool suf
   return suffix ? L - t * tile : min((t + 1) * tile, L);
 }
 
-__global__ void k_sched_zero(int32_t* hist, int32_t n_bins, int32_t* n_items) {
-  for (int32_t i = blockIdx.x * kThreads + threadIdx.x; i < n_bins; i += gridDim.x * kThreads) hist[i] = 0;
-  if (blockIdx.x == 0 && threadIdx.x == 0) *n_items = 0;
-}
-
 __device__ inline int32_t seg_len(const int32_t* cu, int32_t s, int32_t T) {
   const int32_t a = min(max(cu[s], 0), T);
   return min(max(cu[s + 1], a), T) - a;
 }
 
-__global__ void k_sched_count(const int32_t* cu, int32_t n_seg, int32_t T, int32_t tile, int32_t unit, bool suffix,
-                              int32_t* hist, int32_t n_bins) {
-  const int32_t s = blockIdx.x * kThreads + threadIdx.x;
-  if (s >= n_seg) return;
-  const int32_t L = seg_len(cu, s, T);
-  if (L <= 0) return;
-  const int32_t nt = (L + tile - 1) / tile;
-  for (int32_t t = 0; t < nt; ++t) {
-    const int32_t bin = min((tile_work(L, t, tile, suffix) + unit - 1) / unit, n_bins - 1);
-    atomicAdd(&hist[bin], 1);
+// One block: zero the histogram, count each segment's tiles and scan them
+// into toff[0..n_seg] (toff[n_seg] = number of tiles, also stored in n_items).
+__global__ void __launch_bounds__(kThreads) k_sched_tiles(const int32_t* cu, int32_t n_seg, int32_t T, int32_t tile,
+                                                          int32_t* toff, int32_t* hist, int32_t n_bins,
+                                                          int32_t* n_items) {
+  __shared__ int32_t wsum[kThreads / 64];
+  for (int32_t i = threadIdx.x; i < n_bins; i += kThreads) hist[i] = 0;
+  int32_t carry = 0;
+  for (int32_t c = 0; c < n_seg; c += kThreads) {
+    const int32_t s = c + threadIdx.x;
+    int32_t v = 0;
+    if (s < n_seg) v = (seg_len(cu, s, T) + tile - 1) / tile;
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    int32_t x = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int32_t y = __shfl_up(x, o, 64);
+      if (lane >= o) x += y;
+    }
+    if (lane == 63) wsum[wid] = x;
+    __syncthreads();
+    int32_t off = 0, tot = 0;
+    for (int k = 0; k < kThreads / 64; ++k) {
+      if (k < wid) off += wsum[k];
+      tot += wsum[k];
+    }
+    __syncthreads();
+    if (s < n_seg) toff[s] = carry + off + x - v;
+    carry += tot;
+  }
+  if (threadIdx.x == 0) {
+    toff[n_seg] = carry;
+    *n_items = carry;
   }
 }
 
+// Tile i -> (segment, tile index inside it) by binary search over toff.
+__device__ inline void tile_of(const int32_t* toff, int32_t n_seg, int32_t i, int32_t& s, int32_t& t) {
+  int32_t lo = 0, hi = n_seg;  // toff[lo] <= i < toff[hi]
+  while (hi - lo > 1) {
+    const int32_t mid = (lo + hi) >> 1;
+    if (toff[mid] <= i) lo = mid; else hi = mid;
+  }
+  s = lo;
+  t = i - toff[lo];
+}
+
+__device__ inline int32_t tile_bin(const int32_t* cu, int32_t s, int32_t t, int32_t T, int32_t tile, int32_t unit,
+                                   bool suffix, int32_t n_bins) {
+  const int32_t L = seg_len(cu, s, T);
+  return min((tile_work(L, t, tile, suffix) + unit - 1) / unit, n_bins - 1);
+}
+
+__global__ void __launch_bounds__(kThreads) k_sched_count(const int32_t* cu, int32_t n_seg, int32_t T, int32_t tile,
+                                                          int32_t unit, bool suffix, const int32_t* toff,
+                                                          int32_t* hist, int32_t n_bins, int64_t cap) {
+  const int32_t i = blockIdx.x * kThreads + threadIdx.x;
+  const int32_t n = toff[n_seg];
+  if (i >= n || i >= cap) return;
+  int32_t s, t;
+  tile_of(toff, n_seg, i, s, t);
+  atomicAdd(&hist[tile_bin(cu, s, t, T, tile, unit, suffix, n_bins)], 1);
+}
+
 // Descending exclusive scan: cursor[b] = number of tiles in bins > b.
-__global__ void k_sched_scan(int32_t* hist, int32_t n_bins, int32_t* n_items) {
+__global__ void __launch_bounds__(kThreads) k_sched_scan(int32_t* hist, int32_t n_bins) {
   __shared__ int32_t wsum[kThreads / 64];
   int32_t carry = 0;
   for (int32_t c = 0; c < n_bins; c += kThreads) {
@@ -74,23 +122,20 @@ __global__ void k_sched_scan(int32_t* hist, int32_t n_bins, int32_t* n_items) {
     if (i < n_bins) hist[b] = carry + off + x - v;
     carry += tot;
   }
-  if (threadIdx.x == 0) *n_items = carry;
 }
 
-__global__ void k_sched_fill(const int32_t* cu, int32_t n_seg, int32_t T, int32_t tile, int32_t unit, bool suffix,
-                             int32_t* hist, int32_t n_bins, int32_t* items, int64_t cap) {
-  const int32_t s = blockIdx.x * kThreads + threadIdx.x;
-  if (s >= n_seg) return;
-  const int32_t L = seg_len(cu, s, T);
-  if (L <= 0) return;
-  const int32_t nt = (L + tile - 1) / tile;
-  for (int32_t t = 0; t < nt; ++t) {
-    const int32_t bin = min((tile_work(L, t, tile, suffix) + unit - 1) / unit, n_bins - 1);
-    const int32_t pos = atomicAdd(&hist[bin], 1);
-    if (pos < cap) {
-      items[2 * pos] = s;
-      items[2 * pos + 1] = t;
-    }
+__global__ void __launch_bounds__(kThreads) k_sched_fill(const int32_t* cu, int32_t n_seg, int32_t T, int32_t tile,
+                                                         int32_t unit, bool suffix, const int32_t* toff,
+                                                         int32_t* hist, int32_t n_bins, int32_t* items, int64_t cap) {
+  const int32_t i = blockIdx.x * kThreads + threadIdx.x;
+  const int32_t n = toff[n_seg];
+  if (i >= n || i >= cap) return;
+  int32_t s, t;
+  tile_of(toff, n_seg, i, s, t);
+  const int32_t pos = atomicAdd(&hist[tile_bin(cu, s, t, T, tile, unit, suffix, n_bins)], 1);
+  if (pos < cap) {
+    items[2 * pos] = s;
+    items[2 * pos + 1] = t;
   }
 }
 
@@ -103,7 +148,8 @@ static int32_t sched_bins(int32_t max_seqlen, int unit) { return (max_seqlen + u
 
 size_t schedule_bytes(int64_t T, int32_t n_seg, int32_t max_seqlen, int tile, int unit) {
   return align_up(sizeof(int32_t) * 2 * sched_cap(T, n_seg, tile), 256) +
-         align_up(sizeof(int32_t) * sched_bins(max_seqlen, unit), 256) + 256;
+         align_up(sizeof(int32_t) * sched_bins(max_seqlen, unit), 256) +
+         align_up(sizeof(int32_t) * ((size_t)n_seg + 1), 256) + 256;
 }
 
 TileSchedule schedule_carve(void* ws, int64_t T, int32_t n_seg, int32_t max_seqlen, int tile, int unit) {
@@ -115,6 +161,8 @@ TileSchedule schedule_carve(void* ws, int64_t T, int32_t n_seg, int32_t max_seql
   p += align_up(sizeof(int32_t) * 2 * s.cap, 256);
   s.hist = reinterpret_cast<int32_t*>(p);
   p += align_up(sizeof(int32_t) * s.n_bins, 256);
+  s.toff = reinterpret_cast<int32_t*>(p);
+  p += align_up(sizeof(int32_t) * ((size_t)n_seg + 1), 256);
   s.n_items = reinterpret_cast<int32_t*>(p);
   return s;
 }
@@ -122,12 +170,12 @@ TileSchedule schedule_carve(void* ws, int64_t T, int32_t n_seg, int32_t max_seql
 hipError_t launch_schedule(const int32_t* cu, int32_t n_seg, int32_t T, int tile, int unit, bool suffix,
                            const TileSchedule& s, hipStream_t stream) {
   ScopedKernelTimer timed(kTimeSchedule, stream);
-  const unsigned gs = (unsigned)((n_seg + kThreads - 1) / kThreads);
-  k_sched_zero<<<(s.n_bins + kThreads - 1) / kThreads, kThreads, 0, stream>>>(s.hist, s.n_bins, s.n_items);
-  if (n_seg > 0) k_sched_count<<<gs, kThreads, 0, stream>>>(cu, n_seg, T, tile, unit, suffix, s.hist, s.n_bins);
-  k_sched_scan<<<1, kThreads, 0, stream>>>(s.hist, s.n_bins, s.n_items);
-  if (n_seg > 0)
-    k_sched_fill<<<gs, kThreads, 0, stream>>>(cu, n_seg, T, tile, unit, suffix, s.hist, s.n_bins, s.items, s.cap);
+  const unsigned gt = (unsigned)((s.cap + kThreads - 1) / kThreads);
+  k_sched_tiles<<<1, kThreads, 0, stream>>>(cu, n_seg, T, tile, s.toff, s.hist, s.n_bins, s.n_items);
+  k_sched_count<<<gt, kThreads, 0, stream>>>(cu, n_seg, T, tile, unit, suffix, s.toff, s.hist, s.n_bins, s.cap);
+  k_sched_scan<<<1, kThreads, 0, stream>>>(s.hist, s.n_bins);
+  k_sched_fill<<<gt, kThreads, 0, stream>>>(cu, n_seg, T, tile, unit, suffix, s.toff, s.hist, s.n_bins, s.items,
+                                            s.cap);
   return hipGetLastError();
 }
 
