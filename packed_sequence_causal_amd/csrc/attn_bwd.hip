@@ -33,6 +33,7 @@ constexpr int kBQ = 128;   // dQ kernel: query rows per workgroup (4 waves x 32)
 constexpr int kBNq = 64;   // dQ kernel: keys per block
 constexpr int kBKV = 128;  // dK/dV kernel: keys per workgroup (4 waves x 32)
 constexpr int kBMk = 64;   // dK/dV kernel: queries per block
+constexpr int kDkdvValuPerMfma = 4;  // VALU instructions placed after each MFMA of the softmax regions
 
 struct BwdParams {
   const bf16 *q, *k, *v, *o, *dout;
@@ -234,7 +235,8 @@ struct DkvState {
 };
 
 // One 64-query block of the dK/dV loop for one wave (keys wk_lo .. wk_lo+31,
-// this lane's key `key`).
+// this lane's key `key`) that needs the mask: the blocks on the diagonal and
+// the last block of a document.  Unmasked blocks take dkdv_block_full.
 template <int D>
 __device__ __forceinline__ void dkdv_block(DkvState<D>& st, const char* Qs, const char* dOs, const float* l2s,
                                            const float* Ds, int32_t qs, int32_t L, int32_t key, int32_t wk_lo,
@@ -292,6 +294,183 @@ __device__ __forceinline__ void dkdv_block(DkvState<D>& st, const char* Qs, cons
       }
     }
   }
+}
+
+// The unmasked block, software-pipelined inside one wave (at one wave per
+// SIMD nothing else fills the matrix core while a wave waits).  Per 32-query
+// half mq the work is
+//   A(mq): S and dP (16 MFMAs, operand rows read from LDS)
+//   B(mq): P and dS in bf16, laid out as the A operand of the next products
+//   C(mq): dV += P^T dO and dK += dS^T Q (16 MFMAs, column reads from LDS)
+// issued as four regions  A(0) | A(1) + B(0) | C(0) + B(1) | C(1),  so that the
+// VALU work of one half runs between the MFMAs of the other.  Each region
+// ends by reading the first operands of the next one.
+#define PSC_SCHED_BARRIER() __builtin_amdgcn_sched_barrier(0)
+
+__device__ __forceinline__ bf16x8 ld8(const char* p) { return *reinterpret_cast<const bf16x8*>(p); }
+
+// Keeps the computation of x before this point (IR passes otherwise sink
+// arithmetic past a scheduling barrier, next to its first use).
+__device__ __forceinline__ void pin(bf16x8& x) {
+  typedef int i32x4 __attribute__((ext_vector_type(4)));
+  i32x4 t = __builtin_bit_cast(i32x4, x);
+  asm volatile("" : "+v"(t));
+  x = __builtin_bit_cast(bf16x8, t);
+}
+
+template <int D>
+__device__ __forceinline__ void dkdv_block_full(DkvState<D>& st, const char* Qs, const char* dOs, const float* l2s,
+                                                const float* Ds, float c2, int h, int lq, int l) {
+  constexpr int KS = D / 16;
+  constexpr int NC = D / 16;
+  constexpr int PF = 3;  // operands of the next region read ahead
+  const int gi = l & 15;
+  const int dsub = 16 * ((l >> 4) & 1);
+  // A operand of S/dP: row 32*mq + lq, k-step kk
+  auto offA = [&](int mq, int kk) { return lds_byte(32 * mq + lq, 16 * kk + 8 * h); };
+  // B operand of dV/dK, pair c = ks * (D/32) + dt: rows r0, r0 + 8 of column col
+  auto offC0 = [&](int mq, int c) {
+    return lds_byte(32 * mq + 16 * (c / (D / 32)) + 4 * h + (gi >> 2), 32 * (c % (D / 32)) + dsub + 4 * (gi & 3));
+  };
+  auto offC1 = [&](int mq, int c) {
+    return lds_byte(32 * mq + 16 * (c / (D / 32)) + 4 * h + (gi >> 2) + 8, 32 * (c % (D / 32)) + dsub + 4 * (gi & 3));
+  };
+  auto trC = [&](const char* M, int mq, int c) {
+    return tr_read8(reinterpret_cast<const bf16*>(M + offC0(mq, c)), reinterpret_cast<const bf16*>(M + offC1(mq, c)));
+  };
+  auto pds = [&](const f32x16& s, const f32x16& dp, const f32x4* l4, const f32x4* d4, bf16x8* pa, bf16x8* da) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float pr = fast_exp2(__builtin_fmaf(s[i], c2, -l4[i >> 2][i & 3]));
+      pa[i >> 3][i & 7] = (bf16)pr;
+      da[i >> 3][i & 7] = (bf16)(pr * (dp[i] - d4[i >> 2][i & 3]));
+    }
+  };
+
+  // ---------------- region 1: A(0)
+  f32x16 s0 = {}, dp0 = {}, s1 = {}, dp1 = {};
+  bf16x8 nq[KS], nd[KS];        // A(1) operands
+  f32x4 l4a[4], d4a[4];         // B(0) row constants
+  {
+    bf16x8 aq[KS], ad[KS];
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+      aq[kk] = ld8(Qs + offA(0, kk));
+      ad[kk] = ld8(dOs + offA(0, kk));
+    }
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+      s0 = mfma32(aq[kk], st.kf[kk], s0);
+      dp0 = mfma32(ad[kk], st.vf[kk], dp0);
+    }
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      l4a[g] = *reinterpret_cast<const f32x4*>(l2s + 8 * g + 4 * h);
+      d4a[g] = *reinterpret_cast<const f32x4*>(Ds + 8 * g + 4 * h);
+    }
+#pragma unroll
+    for (int kk = 0; kk < PF; ++kk) {
+      nq[kk] = ld8(Qs + offA(1, kk));
+      nd[kk] = ld8(dOs + offA(1, kk));
+    }
+    PSC_SCHED_DS_READ(4);
+#pragma unroll
+    for (int i = 0; i < 2 * KS; ++i) {
+      PSC_SCHED_MFMA(1);
+      PSC_SCHED_DS_READ(1);
+    }
+    PSC_SCHED_DS_READ(8 + 2 * PF);
+  }
+  PSC_SCHED_BARRIER();
+  // ---------------- region 2: A(1) + B(0)
+  bf16x8 pa0[2], da0[2];
+  bf16x8 cb[PF], cq[PF];        // C(0) operands
+  f32x4 l4b[4], d4b[4];         // B(1) row constants
+  {
+#pragma unroll
+    for (int kk = PF; kk < KS; ++kk) {
+      nq[kk] = ld8(Qs + offA(1, kk));
+      nd[kk] = ld8(dOs + offA(1, kk));
+    }
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+      s1 = mfma32(nq[kk], st.kf[kk], s1);
+      dp1 = mfma32(nd[kk], st.vf[kk], dp1);
+    }
+    pds(s0, dp0, l4a, d4a, pa0, da0);
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      l4b[g] = *reinterpret_cast<const f32x4*>(l2s + 32 + 8 * g + 4 * h);
+      d4b[g] = *reinterpret_cast<const f32x4*>(Ds + 32 + 8 * g + 4 * h);
+    }
+#pragma unroll
+    for (int c = 0; c < PF; ++c) {
+      cb[c] = trC(dOs, 0, c);
+      cq[c] = trC(Qs, 0, c);
+    }
+#pragma unroll
+    for (int i = 0; i < 2 * KS; ++i) {
+      PSC_SCHED_MFMA(1);
+      PSC_SCHED_DS_READ(1);
+      PSC_SCHED_VALU(kDkdvValuPerMfma);
+    }
+    PSC_SCHED_DS_READ(8 + 4 * PF);
+  }
+  pin(pa0[0]); pin(pa0[1]); pin(da0[0]); pin(da0[1]);
+  PSC_SCHED_BARRIER();
+  // ---------------- region 3: C(0) + B(1)
+  bf16x8 pa1[2], da1[2];
+  bf16x8 eb[PF], eq[PF];        // C(1) operands
+  {
+    bf16x8 bo[NC], bq[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      bo[c] = c < PF ? cb[c] : trC(dOs, 0, c);
+      bq[c] = c < PF ? cq[c] : trC(Qs, 0, c);
+    }
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const int ks = c / (D / 32), dt = c % (D / 32);
+      st.dva[dt] = mfma32(pa0[ks], bo[c], st.dva[dt]);
+      st.dka[dt] = mfma32(da0[ks], bq[c], st.dka[dt]);
+    }
+    pds(s1, dp1, l4b, d4b, pa1, da1);
+#pragma unroll
+    for (int c = 0; c < PF; ++c) {
+      eb[c] = trC(dOs, 1, c);
+      eq[c] = trC(Qs, 1, c);
+    }
+#pragma unroll
+    for (int i = 0; i < 2 * NC; ++i) {
+      PSC_SCHED_MFMA(1);
+      PSC_SCHED_DS_READ(2);
+      PSC_SCHED_VALU(kDkdvValuPerMfma);
+    }
+  }
+  pin(pa1[0]); pin(pa1[1]); pin(da1[0]); pin(da1[1]);
+  PSC_SCHED_BARRIER();
+  // ---------------- region 4: C(1)
+  {
+    bf16x8 bo[NC], bq[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      bo[c] = c < PF ? eb[c] : trC(dOs, 1, c);
+      bq[c] = c < PF ? eq[c] : trC(Qs, 1, c);
+    }
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const int ks = c / (D / 32), dt = c % (D / 32);
+      st.dva[dt] = mfma32(pa1[ks], bo[c], st.dva[dt]);
+      st.dka[dt] = mfma32(da1[ks], bq[c], st.dka[dt]);
+    }
+    PSC_SCHED_DS_READ(4);
+#pragma unroll
+    for (int i = 0; i < 2 * NC; ++i) {
+      PSC_SCHED_MFMA(1);
+      PSC_SCHED_DS_READ(2);
+    }
+  }
+  PSC_SCHED_BARRIER();
 }
 
 template <int D>
@@ -354,7 +533,10 @@ __global__ void __launch_bounds__(kThreads, 1) k_bwd_dkdv(BwdParams p) {
     if (t + 1 < niter) issue(t + 1, Qs1, dOs1, l2s1, Ds1);
     {
       const int32_t qs = kb + (t % nqb) * kBMk;
-      if (qs + kBMk - 1 >= wk_lo) dkdv_block<D>(st, Qs0, dOs0, l2s0, Ds0, qs, L, key, wk_lo, c2, h, lq, l);
+      if (qs >= wk_lo + 31 && qs + kBMk <= L)
+        dkdv_block_full<D>(st, Qs0, dOs0, l2s0, Ds0, c2, h, lq, l);
+      else if (qs + kBMk - 1 >= wk_lo)
+        dkdv_block<D>(st, Qs0, dOs0, l2s0, Ds0, qs, L, key, wk_lo, c2, h, lq, l);
     }
     if (t + 1 >= niter) break;
     __builtin_amdgcn_s_waitcnt(0);
@@ -362,7 +544,10 @@ __global__ void __launch_bounds__(kThreads, 1) k_bwd_dkdv(BwdParams p) {
     if (t + 2 < niter) issue(t + 2, Qs0, dOs0, l2s0, Ds0);
     {
       const int32_t qs = kb + ((t + 1) % nqb) * kBMk;
-      if (qs + kBMk - 1 >= wk_lo) dkdv_block<D>(st, Qs1, dOs1, l2s1, Ds1, qs, L, key, wk_lo, c2, h, lq, l);
+      if (qs >= wk_lo + 31 && qs + kBMk <= L)
+        dkdv_block_full<D>(st, Qs1, dOs1, l2s1, Ds1, c2, h, lq, l);
+      else if (qs + kBMk - 1 >= wk_lo)
+        dkdv_block<D>(st, Qs1, dOs1, l2s1, Ds1, qs, L, key, wk_lo, c2, h, lq, l);
     }
   }
 
