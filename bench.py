@@ -45,9 +45,9 @@ KERNEL_SOURCES = {
 }
 MEASURED_TRAFFIC = {
     # (kernel, workload): (sources sha256 prefix, read bytes, write bytes)
-    ("attn_fwd", "lognormal_32k"): ("d47bff58d8993a88", 2.0 * 1278509.9 * 1024, 532984.5 * 1024),
-    ("attn_bwd_dkdv", "lognormal_32k"): ("3369b310c6a0abbd", 2.0 * 2712311.2 * 1024, 524288.0 * 1024),
-    ("attn_bwd_dq", "lognormal_32k"): ("3369b310c6a0abbd", 2.0 * 1505341.4 * 1024, 1050031.4 * 1024),
+    ("attn_fwd", "lognormal_32k"): ("0e9143c4ed062ec3", 2.0 * 1380831.0 * 1024, 533027.0 * 1024),
+    ("attn_bwd_dkdv", "lognormal_32k"): ("fb6e14feab08c92c", 2.0 * 4252791.0 * 1024, 524288.0 * 1024),
+    ("attn_bwd_dq", "lognormal_32k"): ("fb6e14feab08c92c", 2.0 * 1624388.8 * 1024, 1055073.9 * 1024),
 }
 
 
