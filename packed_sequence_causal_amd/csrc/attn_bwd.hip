@@ -156,7 +156,8 @@ __global__ void __launch_bounds__(kThreads, 2) k_bwd_dq(BwdParams p) {
   __shared__ __attribute__((aligned(16))) char Ks1[tile_bytes<D>()];
   __shared__ __attribute__((aligned(16))) char Vs1[tile_bytes<D>()];
 
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, h = l >> 5, lq = l & 31;
+  const int tid = threadIdx.x, l = tid & 63, h = l >> 5, lq = l & 31;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const uint32_t b = xcd_group_remap(blockIdx.x, gridDim.x, (uint32_t)p.group);
   const uint32_t item = b / (uint32_t)p.hq, head = b % (uint32_t)p.hq;
   if ((int32_t)item >= *p.n_items) return;
@@ -171,8 +172,11 @@ __global__ void __launch_bounds__(kThreads, 2) k_bwd_dq(BwdParams p) {
   const bf16* Vp = p.v + (int64_t)s0 * p.sv + (int64_t)kvh * D;
   const int32_t kv_end = min(q0 + kBQ, L);
   const int32_t nkv = (kv_end + kBNq - 1) / kBNq;
-  load_tile_async<D, kThreads / 64>(Kp, p.sk, 0, L, Ks0, w, l);
-  load_tile_async<D, kThreads / 64>(Vp, p.sv, 0, L, Vs0, w, l);
+  uint32_t koff[D / 8 / (kThreads / 64)], voff[D / 8 / (kThreads / 64)];
+  tile_offsets<D, kThreads / 64>(p.sk, w, l, koff);
+  tile_offsets<D, kThreads / 64>(p.sv, w, l, voff);
+  load_tile<D, kThreads / 64>(Kp, p.sk, 0, L, koff, Ks0, w, l);
+  load_tile<D, kThreads / 64>(Vp, p.sv, 0, L, voff, Vs0, w, l);
 
   const int32_t qrow = q0 + 32 * w + lq;
   const bool qvalid = qrow < L;
@@ -197,16 +201,16 @@ __global__ void __launch_bounds__(kThreads, 2) k_bwd_dq(BwdParams p) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (j + 1 < nkv) {
-      load_tile_async<D, kThreads / 64>(Kp, p.sk, (j + 1) * kBNq, L, Ks1, w, l);
-      load_tile_async<D, kThreads / 64>(Vp, p.sv, (j + 1) * kBNq, L, Vs1, w, l);
+      load_tile<D, kThreads / 64>(Kp, p.sk, (j + 1) * kBNq, L, koff, Ks1, w, l);
+      load_tile<D, kThreads / 64>(Vp, p.sv, (j + 1) * kBNq, L, voff, Vs1, w, l);
     }
     if (j * kBNq <= wq_hi) dq_block<D>(st, Ks0, Vs0, j * kBNq, L, qrow, wq_lo, c2, h, lq, l);
     if (j + 1 >= nkv) break;
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (j + 2 < nkv) {
-      load_tile_async<D, kThreads / 64>(Kp, p.sk, (j + 2) * kBNq, L, Ks0, w, l);
-      load_tile_async<D, kThreads / 64>(Vp, p.sv, (j + 2) * kBNq, L, Vs0, w, l);
+      load_tile<D, kThreads / 64>(Kp, p.sk, (j + 2) * kBNq, L, koff, Ks0, w, l);
+      load_tile<D, kThreads / 64>(Vp, p.sv, (j + 2) * kBNq, L, voff, Vs0, w, l);
     }
     if ((j + 1) * kBNq <= wq_hi) dq_block<D>(st, Ks1, Vs1, (j + 1) * kBNq, L, qrow, wq_lo, c2, h, lq, l);
   }
@@ -503,8 +507,7 @@ __global__ void __launch_bounds__(kThreads, 1) k_bwd_dkdv(BwdParams p) {
     const int32_t head = kvh * p.group + t / nqb;
     const int32_t qs = kb + (t % nqb) * kBMk;
     load_tile_async<D, kThreads / 64>(p.q + (int64_t)s0 * p.sq + (int64_t)head * D, p.sq, qs, L, Qs, w, l);
-    load_tile_async<D, kThreads / 64>(p.dout + (int64_t)s0 * p.sdo + (int64_t)head * D, p.sdo, qs, L, dOs,
-                                           w, l);
+    load_tile_async<D, kThreads / 64>(p.dout + (int64_t)s0 * p.sdo + (int64_t)head * D, p.sdo, qs, L, dOs, w, l);
     if (w == 0) load_vec64_async(p.L2buf + (int64_t)head * p.T + s0, qs, L, l2s, l);
     if (w == 1) load_vec64_async(p.Dbuf + (int64_t)head * p.T + s0, qs, L, Ds, l);
   };

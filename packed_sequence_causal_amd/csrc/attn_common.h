@@ -84,6 +84,14 @@ __device__ __forceinline__ uint32_t xcd_group_remap(uint32_t b, uint32_t n, uint
 __device__ __forceinline__ void lds_dma16(const void* src, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(src) : "memory", "m0");
 }
+// lds_dma16 with a uniform 64-bit base (SGPRs) and a 32-bit per-lane byte
+// offset: the address needs no per-lane arithmetic.
+__device__ __forceinline__ void lds_dma16_sv(const void* sbase, uint32_t voff, uint32_t lds) {
+  const uint64_t a = (uint64_t)(uintptr_t)sbase;
+  const uint64_t b = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32)) << 32) |
+                     (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a);
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(voff), "s"(b) : "memory", "m0");
+}
 __device__ __forceinline__ void lds_dma4(const void* src, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" ::"s"(lds), "v"(src) : "memory", "m0");
 }
@@ -147,6 +155,49 @@ __device__ __forceinline__ void load_tile_async(const bf16* base, int64_t stride
     const bf16* src = base + (int64_t)min(row0 + r, L - 1) * stride + c * 8;
     lds_dma16(src, lds0 + (tu >> 3) * kGroupBytes + (tu & 7) * 1024);
   }
+}
+
+// Per-lane byte offsets (from the tile's first row) of the chunks this wave
+// fetches in load_tile_async, for a tile that needs no row clamping.
+// stride * 128 must stay below 2^32 (checked by the host API).
+template <int D, int NW>
+__device__ __forceinline__ void tile_offsets(int64_t stride, int w, int l, uint32_t* off) {
+  constexpr int LOADS = D / 8;
+  const int rr = l >> 3;
+  const int p = l & 7;
+#pragma unroll
+  for (int i = 0; i < LOADS / NW; ++i) {
+    const int t = w + NW * i;
+    const int g = t >> 3;
+    const int r = 8 * (t & 7) + rr;
+    const int c = 8 * g + (p ^ lds_swz(r));
+    off[i] = (uint32_t)(((int64_t)r * stride + c * 8) * 2);
+  }
+}
+
+// load_tile_async for rows [row0, row0 + 64) all inside the segment; `rows`
+// points at row row0 (wave-uniform), `off` from tile_offsets.
+template <int D, int NW>
+__device__ __forceinline__ void load_tile_async_full(const bf16* rows, const uint32_t* off, void* lds, int w) {
+  constexpr int LOADS = D / 8;
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  const uint32_t lds0 = lds_addr(lds);
+#pragma unroll
+  for (int i = 0; i < LOADS / NW; ++i) {
+    const int tu = wu + NW * i;
+    lds_dma16_sv(rows, off[i], lds0 + (tu >> 3) * kGroupBytes + (tu & 7) * 1024);
+  }
+}
+
+// load_tile_async with the offset-only fast path for tiles inside the
+// segment (`off` from tile_offsets for this stride).
+template <int D, int NW>
+__device__ __forceinline__ void load_tile(const bf16* base, int64_t stride, int32_t row0, int32_t L,
+                                          const uint32_t* off, void* lds, int w, int l) {
+  if (row0 + kTileRows <= L)
+    load_tile_async_full<D, NW>(base + (int64_t)row0 * stride, off, lds, w);
+  else
+    load_tile_async<D, NW>(base, stride, row0, L, lds, w, l);
 }
 
 // Asynchronous load of 64 consecutive floats vec[row0 .. row0 + 64) (rows at or

@@ -50,9 +50,10 @@ struct FwdParams {
 // Asynchronous loads of key/value rows [kb, kb + 64) into one LDS stage.
 template <int D>
 __device__ __forceinline__ void load_kv(const bf16* Kp, const bf16* Vp, int64_t sk, int64_t sv, int32_t kb,
-                                        int32_t L, char* Ks, char* Vs, int w, int l) {
-  load_tile_async<D, kThreads / 64>(Kp, sk, kb, L, Ks, w, l);
-  load_tile_async<D, kThreads / 64>(Vp, sv, kb, L, Vs, w, l);
+                                        int32_t L, char* Ks, char* Vs, const uint32_t* koff, const uint32_t* voff,
+                                        int w, int l) {
+  load_tile<D, kThreads / 64>(Kp, sk, kb, L, koff, Ks, w, l);
+  load_tile<D, kThreads / 64>(Vp, sv, kb, L, voff, Vs, w, l);
 }
 
 template <int D>
@@ -131,7 +132,8 @@ __global__ void __launch_bounds__(kThreads, 2) k_attn_fwd(FwdParams p) {
   __shared__ __attribute__((aligned(16))) char Ks1[tile_bytes<D>()];
   __shared__ __attribute__((aligned(16))) char Vs1[tile_bytes<D>()];
 
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, h = l >> 5, lq = l & 31;
+  const int tid = threadIdx.x, l = tid & 63, h = l >> 5, lq = l & 31;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const uint32_t b = xcd_group_remap(blockIdx.x, gridDim.x, (uint32_t)p.group);
   const uint32_t item = b / (uint32_t)p.hq, head = b % (uint32_t)p.hq;
   if ((int32_t)item >= *p.n_items) return;
@@ -150,7 +152,10 @@ __global__ void __launch_bounds__(kThreads, 2) k_attn_fwd(FwdParams p) {
 
   const int32_t kv_end = min(q0 + kBM, L);
   const int32_t nkv = (kv_end + kBN - 1) / kBN;
-  load_kv<D>(Kp, Vp, p.sk, p.sv, 0, L, Ks0, Vs0, w, l);
+  uint32_t koff[D / 8 / (kThreads / 64)], voff[D / 8 / (kThreads / 64)];
+  tile_offsets<D, kThreads / 64>(p.sk, w, l, koff);
+  tile_offsets<D, kThreads / 64>(p.sv, w, l, voff);
+  load_kv<D>(Kp, Vp, p.sk, p.sv, 0, L, Ks0, Vs0, koff, voff, w, l);
 
   const int32_t qrow = q0 + 32 * w + lq;
   const bool qvalid = qrow < L;
@@ -171,13 +176,13 @@ __global__ void __launch_bounds__(kThreads, 2) k_attn_fwd(FwdParams p) {
     // stage 0 holds block j
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (j + 1 < nkv) load_kv<D>(Kp, Vp, p.sk, p.sv, (j + 1) * kBN, L, Ks1, Vs1, w, l);
+    if (j + 1 < nkv) load_kv<D>(Kp, Vp, p.sk, p.sv, (j + 1) * kBN, L, Ks1, Vs1, koff, voff, w, l);
     if (j * kBN <= wq_hi) fwd_block<D>(st, Ks0, Vs0, j * kBN, L, qrow, wq_lo, c2, h, lq, l);
     if (j + 1 >= nkv) break;
     // stage 1 holds block j + 1
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (j + 2 < nkv) load_kv<D>(Kp, Vp, p.sk, p.sv, (j + 2) * kBN, L, Ks0, Vs0, w, l);
+    if (j + 2 < nkv) load_kv<D>(Kp, Vp, p.sk, p.sv, (j + 2) * kBN, L, Ks0, Vs0, koff, voff, w, l);
     if ((j + 1) * kBN <= wq_hi) fwd_block<D>(st, Ks1, Vs1, (j + 1) * kBN, L, qrow, wq_lo, c2, h, lq, l);
   }
 

@@ -60,6 +60,8 @@ bool operand_ok(const void* p, int64_t tok_stride, int32_t heads, int32_t d, int
   if (dtype == PSC_BF16) {
     if (reinterpret_cast<uintptr_t>(p) % 16 != 0) return false;
     if ((tok_stride * 2) % 16 != 0) return false;
+    // the bf16 kernels address a 64-row tile with 32-bit byte offsets
+    if (tok_stride > ((int64_t)1 << 25)) return false;
   } else {
     if (reinterpret_cast<uintptr_t>(p) % 4 != 0) return false;
   }

@@ -106,6 +106,7 @@ def _fwd_raw(**kw):
     (dict(q=8), psc.ERR_INVALID),                # misaligned base for bf16
     (dict(sq=200), psc.ERR_INVALID),             # stride below heads*D
     (dict(sk=130), psc.ERR_INVALID),             # stride*2 not a multiple of 16 bytes
+    (dict(sv=(1 << 25) + 8), psc.ERR_INVALID),   # a 64-row bf16 tile would need byte offsets >= 2^32
     (dict(cu=None), psc.ERR_INVALID),
     (dict(lse=None), psc.ERR_INVALID),
     (dict(nseg=0), psc.ERR_INVALID),
