@@ -192,6 +192,42 @@ def _layout(w):
     return np.asarray(pack_ref.flatten(rows, p.packed_length)["cu_seqlens"], dtype=np.int32)
 
 
+def sampled_check(q, k, v, do, cu, a_hq, a_hkv, dtype, backward, got, seed=1):
+    """Sampled comparison with the oracle at full size: random rows and the
+    tail of the longest document (o, lse, dq), the last keys of the longest
+    document (dk, dv for one kv head) and two whole short documents."""
+    T = int(cu[-1])
+    rng = np.random.default_rng(seed)
+    lens = np.diff(cu)
+    longest = int(np.argmax(lens))
+    s_long, e_long = int(cu[longest]), int(cu[longest + 1])
+    rows = np.concatenate([rng.integers(0, T, 96), np.arange(e_long - 32, e_long)])
+    heads = rng.integers(0, a_hq, rows.size)
+    o, lse = attn_ref.attn_rows(q, k, v, cu, rows, heads)
+    close("o", got["o"][rows, heads].numpy(), o, dtype)
+    close("lse", got["lse"][heads, rows].numpy(), lse, dtype)
+    if not backward:
+        return
+    dq = attn_ref.attn_rows_dq(q, k, v, do, cu, rows[:64], heads[:64])
+    close("dq", got["dq"][rows[:64], heads[:64]].numpy(), dq, dtype)
+    g = int(rng.integers(0, a_hkv))
+    key_lo = max(s_long, e_long - 160)
+    dk, dv = attn_ref.attn_bwd_keys(q, k, v, do, cu, longest, key_lo, [g])
+    close("dk tail", got["dk"][key_lo:e_long, [g]].numpy(), dk, dtype)
+    close("dv tail", got["dv"][key_lo:e_long, [g]].numpy(), dv, dtype)
+    short = [i for i in np.argsort(lens) if lens[i] > 8][:2]
+    if len(lens) < 2:
+        return
+    heads_kv = list(range(a_hkv))
+    for si in short:
+        s, e = int(cu[si]), int(cu[si + 1])
+        if e - s > 4096:
+            continue  # whole-document key gradients only for short documents
+        dk, dv = attn_ref.attn_bwd_keys(q, k, v, do, cu, int(si), s, heads_kv)
+        close("dk doc", got["dk"][s:e].numpy(), dk, dtype)
+        close("dv doc", got["dv"][s:e].numpy(), dv, dtype)
+
+
 @pytest.mark.parametrize("name", ["uniform_8k", "lognormal_32k", "seqpar_share_128k", "skewed_32k"])
 def test_full_size_sampled(name):
     w = workloads.make(name)
@@ -201,31 +237,17 @@ def test_full_size_sampled(name):
     q, k, v, do = workloads.qkv_do(T, a.hq, a.hkv, a.head_dim, seed=0, dtype=a.dtype)
     print(f"[{name}] T={T} segments={len(cu) - 1} hq={a.hq} hkv={a.hkv} D={a.head_dim}", flush=True)
     got = run(q, k, v, do, cu, backward=a.backward)
-    rng = np.random.default_rng(1)
-    lens = np.diff(cu)
-    longest = int(np.argmax(lens))
-    s_long, e_long = int(cu[longest]), int(cu[longest + 1])
-    # random rows plus the tail of the longest document (its longest key ranges)
-    rows = np.concatenate([rng.integers(0, T, 96), np.arange(e_long - 32, e_long)])
-    heads = rng.integers(0, a.hq, rows.size)
-    o, lse = attn_ref.attn_rows(q, k, v, cu, rows, heads)
-    close("o", got["o"][rows, heads].numpy(), o, a.dtype)
-    close("lse", got["lse"][heads, rows].numpy(), lse, a.dtype)
-    if not a.backward:
-        return
-    dq = attn_ref.attn_rows_dq(q, k, v, do, cu, rows[:64], heads[:64])
-    close("dq", got["dq"][rows[:64], heads[:64]].numpy(), dq, a.dtype)
-    # dK/dV: the last keys of the longest document (one kv head), and two
-    # whole short documents (every kv head)
-    g = int(rng.integers(0, a.hkv))
-    key_lo = max(s_long, e_long - 160)
-    dk, dv = attn_ref.attn_bwd_keys(q, k, v, do, cu, longest, key_lo, [g])
-    close("dk tail", got["dk"][key_lo:e_long, [g]].numpy(), dk, a.dtype)
-    close("dv tail", got["dv"][key_lo:e_long, [g]].numpy(), dv, a.dtype)
-    short = [i for i in np.argsort(lens) if lens[i] > 8][:2]
-    heads_kv = list(range(a.hkv))
-    for si in short:
-        s, e = int(cu[si]), int(cu[si + 1])
-        dk, dv = attn_ref.attn_bwd_keys(q, k, v, do, cu, int(si), s, heads_kv)
-        close("dk doc", got["dk"][s:e].numpy(), dk, a.dtype)
-        close("dv doc", got["dv"][s:e].numpy(), dv, a.dtype)
+    sampled_check(q, k, v, do, cu, a.hq, a.hkv, a.dtype, a.backward, got)
+
+
+# The document-length sweep's rows (one 32768-token row, GQA 32/8, D 128):
+# with the document mask and as one whole-row causal segment.
+@pytest.mark.parametrize("name,whole_row", [("16K+16K", False), ("2K+30K", False), ("2K+30K", True),
+                                            ("32x1K", False)])
+def test_doc_sweep_layouts_sampled(name, whole_row):
+    cu = workloads.doc_sweep_cu(name, whole_row)
+    T = int(cu[-1])
+    q, k, v, do = workloads.qkv_do(T, 32, 8, 128, seed=0, dtype="bf16")
+    print(f"[sweep {name} whole_row={whole_row}] T={T} segments={len(cu) - 1}", flush=True)
+    got = run(q, k, v, do, cu, backward=True)
+    sampled_check(q, k, v, do, cu, 32, 8, "bf16", True, got)

@@ -234,3 +234,28 @@ def random_layout(rng, total, lo, hi):
     off = np.zeros(len(lens) + 1, dtype=np.int32)
     off[1:] = np.cumsum(lens)
     return off
+
+
+# Document layouts of one 32768-token row for the document-length sweep: the
+# three named on the Sample Packing page (section 5.3: one 32K document,
+# 16K + 16K, 2K + 30K) and further splits, longest document from S to S/32.
+DOC_SWEEP_ROW = 32768
+DOC_SWEEP = {
+    "32K": [32768],
+    "30K+2K": [30720, 2048],
+    "2K+30K": [2048, 30720],
+    "24K+8K": [24576, 8192],
+    "16K+16K": [16384, 16384],
+    "4x8K": [8192] * 4,
+    "8x4K": [4096] * 8,
+    "16x2K": [2048] * 16,
+    "32x1K": [1024] * 32,
+}
+
+
+def doc_sweep_cu(name: str, whole_row: bool = False) -> np.ndarray:
+    """cu_seqlens of a sweep layout, or of the same row as one causal segment."""
+    lens = [DOC_SWEEP_ROW] if whole_row else DOC_SWEEP[name]
+    assert sum(lens) == DOC_SWEEP_ROW
+    return np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+
