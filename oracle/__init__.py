@@ -11,6 +11,8 @@ Contents:
   dense_ref  fp64 attention on the whole row under a dense block-diagonal causal
              mask built the Megatron way (tiny inputs only)
   mask_stats block sparsity of the document-causal mask
+  rope_ref   fp64 rotary position embedding of packed rows (positions from
+             the packer's indexes)
 
 Every function is pinned by tests under ``tests/test_oracle_*.py`` to values the
 pages print, to closed forms, to library routines on special cases, or to brute
