@@ -154,6 +154,34 @@ def cpu_baseline(w, q, k, v, do, cu, real, budget_s):
     }
 
 
+def rope_rate(psc, torch, np, qd, kd, pk, w, args):
+    """Rotary embedding of the workload's q and k in place (positions = the
+    packer's indexes), timed apart from the step: HBM-bound, algorithmic bytes
+    = q and k read and written once + positions."""
+    T, hq, D = qd.shape
+    hkv = kd.shape[1]
+    pos = pk["indexes"][: w.pack.keep_rows].reshape(-1)[:T].contiguous()
+    if pos.numel() != T:
+        return None
+    q2, k2 = qd.clone(), kd.clone()
+    for _ in range(3):
+        psc.rope(q2, k2, pos)
+    torch.cuda.synchronize()
+    psc.timing_reset()
+    psc.timing_enable(True)
+    n = 20
+    for _ in range(n):
+        psc.rope(q2, k2, pos)
+    torch.cuda.synchronize()
+    psc.timing_enable(False)
+    ms_total, launches = psc.timing_read()["rope"]
+    ms = ms_total / max(launches, 1)
+    nbytes = 2 * (q2.numel() + k2.numel()) * q2.element_size() + 4 * T
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"kernel": "rope", "bound": "hbm", "ms": round(ms, 4), "bytes": nbytes, "achieved": round(gbs, 1),
+            "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "launches": launches}
+
+
 def doc_sweep(args):
     """The Sample Packing page's document-length measurement (section 5.3) on
     this kernel: each layout of one 32768-token row with its document mask,
@@ -365,6 +393,7 @@ def main():
         result["bwd"] = {"ms": round(bwd_ms, 4), "min_ms": round(float(min(bwd_all)), 4),
                          "tflops": round(bwd_flops / (bwd_ms * 1e-3) / 1e12, 2),
                          "pct_peak": round(100 * bwd_flops / (bwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2)}
+    result["rope"] = rope_rate(psc, torch, np, qd, kd, pk, w, args)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, q, k, v, do, cu_h, real, args.cpu_seconds)
     print(json.dumps(result), flush=True)

@@ -131,6 +131,32 @@ int psc_pack_build(int mode, const int32_t* tokens, const int64_t* doc_offsets,
                    size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ */
+/* Rotary position embedding from the packer's indexes                      */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * psc_rope — rotate q [T, hq, D] and k [T, hkv, D] in place by the position of
+ * each token inside its document, positions[t] (int32 [T]; the packer's
+ * `indexes`, which restart at 0 in every segment: InternEvo "数据加载与流程",
+ * section "获取Dataloader数据").  Dims i and i + D/2 (i < D/2) of every head
+ * turn by theta_i = positions[t] * base^(-2i/D):
+ *   x_i' = x_i cos - x_{i+D/2} sin,   x_{i+D/2}' = x_{i+D/2} cos + x_i sin,
+ * the rotate-half form of apply_rotary_pos_emb(q, k, cos, sin) (XTuner
+ * sequence-parallel page, section "实现方案").  inverse != 0 turns by -theta
+ * (the backward pass: it maps dq', dk' to the gradients of q, k).
+ * The angle is reduced modulo 2*pi in fp64, products are fp32, results are
+ * rounded to `dtype` once.  Addressing: base + t*tok_stride + h*D + d
+ * (elements); base and tok_stride*sizeof(element) must be multiples of 16
+ * bytes.  k may be NULL (then hkv is ignored).  head_dim: 32, 64, 128 for
+ * both dtypes; base > 0 and finite.
+ * Errors: PSC_ERR_INVALID (null q or positions, alignment, stride below
+ * heads*D, bad base), PSC_ERR_UNSUPPORTED (head_dim), PSC_ERR_HIP.
+ */
+int psc_rope(int dtype, void* q, int64_t q_tok_stride, int32_t hq, void* k, int64_t k_tok_stride,
+             int32_t hkv, int64_t total_tokens, int32_t head_dim, const int32_t* positions, float base,
+             int inverse, void* stream);
+
+/* ------------------------------------------------------------------------ */
 /* Document-causal attention                                                 */
 /* ------------------------------------------------------------------------ */
 
@@ -208,7 +234,8 @@ typedef enum psc_kernel {
   PSC_K_ATTN_FWD = 2,
   PSC_K_ATTN_BWD_PRE = 3,
   PSC_K_ATTN_BWD_DKDV = 4,
-  PSC_K_ATTN_BWD_DQ = 5
+  PSC_K_ATTN_BWD_DQ = 5,
+  PSC_K_ROPE = 6
 } psc_kernel;
 
 int psc_timing_enable(int enable);

@@ -57,6 +57,9 @@ _SIGNATURES = {
                                            ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32,
                                            ctypes.c_int32, ctypes.c_int32, ctypes.c_float, _vp, _vp, _vp, _vp,
                                            ctypes.c_size_t, _vp]),
+    "psc_rope": (ctypes.c_int, [ctypes.c_int, _vp, ctypes.c_int64, ctypes.c_int32, _vp, ctypes.c_int64,
+                                ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, _vp, ctypes.c_float, ctypes.c_int,
+                                _vp]),
 }
 
 
@@ -231,7 +234,24 @@ def varlen_attn_bwd(q, k, v, out, dout, lse, cu_seqlens, max_seqlen: int, n_segm
 
 # ---------------------------------------------------------- instrumentation
 
-KERNELS = {"pack": 0, "attn_schedule": 1, "attn_fwd": 2, "attn_bwd_pre": 3, "attn_bwd_dkdv": 4, "attn_bwd_dq": 5}
+def rope(q, k, positions, base: float = 10000.0, inverse: bool = False, stream=None):
+    """Rotate q [T,hq,D] and k [T,hkv,D] (or None) in place by positions int32
+    [T] (the packer's indexes); inverse=True applies the backward rotation.
+    Returns (q, k)."""
+    T, hq, D = q.shape
+    hkv = 0 if k is None else k.shape[1]
+    if k is not None and (k.shape[0] != T or k.shape[2] != D or k.dtype != q.dtype):
+        raise ValueError("q and k must agree in tokens, head dim and dtype")
+    if positions.numel() != T:
+        raise ValueError("positions must have one entry per token")
+    _check(lib().psc_rope(_dtype_code(q), _ptr(q), _tok_stride(q, "q"), hq, _ptr(k),
+                          0 if k is None else _tok_stride(k, "k"), hkv, T, D, _ptr(positions), float(base),
+                          1 if inverse else 0, _stream(stream)), "psc_rope")
+    return q, k
+
+
+KERNELS = {"pack": 0, "attn_schedule": 1, "attn_fwd": 2, "attn_bwd_pre": 3, "attn_bwd_dkdv": 4, "attn_bwd_dq": 5,
+           "rope": 6}
 
 
 def timing_enable(on: bool = True):

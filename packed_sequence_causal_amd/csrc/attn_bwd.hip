@@ -502,12 +502,15 @@ __global__ void __launch_bounds__(kThreads, 1) k_bwd_dkdv(BwdParams p) {
   const int32_t nqb = (L - kb + kBMk - 1) / kBMk;
   const int32_t niter = p.group * nqb;
 
+  uint32_t qoff[D / 8 / (kThreads / 64)], ooff[D / 8 / (kThreads / 64)];
+  tile_offsets<D, kThreads / 64>(p.sq, w, l, qoff);
+  tile_offsets<D, kThreads / 64>(p.sdo, w, l, ooff);
   // iteration t: query head kvh*G + t / nqb, query block kb + (t % nqb) * 64
   auto issue = [&](int32_t t, char* Qs, char* dOs, float* l2s, float* Ds) {
     const int32_t head = kvh * p.group + t / nqb;
     const int32_t qs = kb + (t % nqb) * kBMk;
-    load_tile_async<D, kThreads / 64>(p.q + (int64_t)s0 * p.sq + (int64_t)head * D, p.sq, qs, L, Qs, w, l);
-    load_tile_async<D, kThreads / 64>(p.dout + (int64_t)s0 * p.sdo + (int64_t)head * D, p.sdo, qs, L, dOs, w, l);
+    load_tile<D, kThreads / 64>(p.q + (int64_t)s0 * p.sq + (int64_t)head * D, p.sq, qs, L, qoff, Qs, w, l);
+    load_tile<D, kThreads / 64>(p.dout + (int64_t)s0 * p.sdo + (int64_t)head * D, p.sdo, qs, L, ooff, dOs, w, l);
     if (w == 0) load_vec64_async(p.L2buf + (int64_t)head * p.T + s0, qs, L, l2s, l);
     if (w == 1) load_vec64_async(p.Dbuf + (int64_t)head * p.T + s0, qs, L, Ds, l);
   };

@@ -233,4 +233,37 @@ int psc_varlen_attn_bwd(int dtype, const void* q, const void* k, const void* v, 
   return e == hipSuccess ? PSC_OK : PSC_ERR_HIP;
 }
 
+int psc_rope(int dtype, void* q, int64_t q_tok_stride, int32_t hq, void* k, int64_t k_tok_stride, int32_t hkv,
+             int64_t total_tokens, int32_t head_dim, const int32_t* positions, float base, int inverse,
+             void* stream) {
+  if (dtype != PSC_F32 && dtype != PSC_BF16) return PSC_ERR_INVALID;
+  const int64_t T = total_tokens;
+  if (T < 0 || T > kI32Max || hq < 1 || (k && hkv < 1)) return PSC_ERR_INVALID;
+  if (!(base > 0.f) || std::isinf(base)) return PSC_ERR_INVALID;
+  if (head_dim != 32 && head_dim != 64 && head_dim != 128) return PSC_ERR_UNSUPPORTED;
+  if (T == 0) return PSC_OK;
+  const int64_t esize = dtype == PSC_BF16 ? 2 : 4;
+  auto ok = [&](const void* p, int64_t stride, int32_t heads) {
+    if (!p || stride < (int64_t)heads * head_dim) return false;
+    return reinterpret_cast<uintptr_t>(p) % 16 == 0 && (stride * esize) % 16 == 0;
+  };
+  if (!ok(q, q_tok_stride, hq) || (k && !ok(k, k_tok_stride, hkv)) || !positions) return PSC_ERR_INVALID;
+  psc::RopeArgs a;
+  a.dtype = dtype;
+  a.q = q;
+  a.k = k;
+  a.sq = q_tok_stride;
+  a.sk = k ? k_tok_stride : 0;
+  a.T = T;
+  a.hq = hq;
+  a.hkv = k ? hkv : 0;
+  a.d = head_dim;
+  a.inverse = inverse != 0;
+  a.pos = positions;
+  for (int i = 0; i < 64; ++i)
+    a.inv_freq[i] = i < head_dim / 2 ? std::pow((double)base, -2.0 * i / head_dim) : 0.0;
+  const hipError_t e = psc::launch_rope(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PSC_OK : PSC_ERR_HIP;
+}
+
 }  // extern "C"

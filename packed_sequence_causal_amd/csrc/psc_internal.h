@@ -9,7 +9,7 @@
 namespace psc {
 
 // Kernel timing slots (numbering matches enum psc_kernel in psc.h).
-enum TimerSlot { kTimePack = 0, kTimeSchedule, kTimeFwd, kTimeBwdPre, kTimeBwdDkdv, kTimeBwdDq, kTimerSlots };
+enum TimerSlot { kTimePack = 0, kTimeSchedule, kTimeFwd, kTimeBwdPre, kTimeBwdDkdv, kTimeBwdDq, kTimeRope, kTimerSlots };
 
 // Brackets the launches made during its lifetime with HIP events on `stream`
 // when timing is switched on (timing.hip); does nothing otherwise.
@@ -105,5 +105,18 @@ hipError_t launch_attn_fwd_bf16(const AttnFwdArgs& a, hipStream_t stream);
 hipError_t launch_attn_bwd_bf16(const AttnBwdArgs& a, hipStream_t stream);
 hipError_t launch_attn_fwd_f32(const AttnFwdArgs& a, hipStream_t stream);
 hipError_t launch_attn_bwd_f32(const AttnBwdArgs& a, hipStream_t stream);
+
+// Rotary embedding of q [T, hq, D] and k [T, hkv, D] in place (k may be null).
+struct RopeArgs {
+  int dtype;  // psc_dtype
+  void* q;
+  void* k;
+  int64_t sq, sk, T;
+  int32_t hq, hkv, d;
+  int32_t inverse;
+  const int32_t* pos;
+  double inv_freq[64];  // base^(-2i/D), i < D/2
+};
+hipError_t launch_rope(const RopeArgs& a, hipStream_t stream);
 
 }  // namespace psc

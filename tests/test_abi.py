@@ -146,3 +146,36 @@ def test_attn_workspace_sizes():
     assert bwd >= 4 * 32 * 65536  # D row sums in fp32
     with pytest.raises(psc.PscError):
         psc.varlen_attn_workspace(2, psc.BF16, 16, 1, 16, 2, 1, 128)
+
+
+def _rope_raw(**kw):
+    a = dict(dtype=psc.BF16, q=16, sq=256, hq=2, k=16, sk=128, hkv=1, T=16, D=128, pos=16, base=10000.0, inv=0)
+    a.update(kw)
+    v = lambda x: None if x is None else ctypes.c_void_p(x)
+    return psc.lib().psc_rope(a["dtype"], v(a["q"]), a["sq"], a["hq"], v(a["k"]), a["sk"], a["hkv"], a["T"],
+                              a["D"], v(a["pos"]), a["base"], a["inv"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=7), psc.ERR_INVALID),
+    (dict(q=None), psc.ERR_INVALID),
+    (dict(pos=None), psc.ERR_INVALID),
+    (dict(q=24), psc.ERR_INVALID),             # q not 16-byte aligned
+    (dict(sq=200), psc.ERR_INVALID),           # stride below heads*D
+    (dict(dtype=psc.F32, sq=258), psc.ERR_INVALID),  # stride*4 not a multiple of 16 bytes
+    (dict(k=16, hkv=0), psc.ERR_INVALID),
+    (dict(base=0.0), psc.ERR_INVALID),
+    (dict(base=-2.0), psc.ERR_INVALID),
+    (dict(base=float("inf")), psc.ERR_INVALID),
+    (dict(base=float("nan")), psc.ERR_INVALID),
+    (dict(D=96), psc.ERR_UNSUPPORTED),
+    (dict(T=-1), psc.ERR_INVALID),
+])
+def test_rope_rejects_on_host(kw, code):
+    assert _rope_raw(**kw) == code
+
+
+def test_rope_empty_is_a_no_op():
+    assert _rope_raw(T=0, q=None, k=None, pos=None) == 0
+    assert _rope_raw(T=0) == 0
+
