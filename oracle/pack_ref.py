@@ -7,7 +7,8 @@ Source: InternEvo documentation, page "数据加载与流程" (data flow):
     (micro_bsz 2, SEQ_LEN 8) for build_pack and build_unpack, and the label rule;
   * section "获取Dataloader数据": the batch contract (input_ids, cu_seqlens,
     indexes, label) with the same example's cu_seqlens and indexes;
-  * section "处理数据": packed_data_normalizer's max_seqlen, and unpack_data.
+  * section "处理数据": packed_data_normalizer's max_seqlen, unpack_data and
+    split_data_sequence_parallel (tp = 2 examples for packed and unpacked data).
 
 Readings taken where the page is silent (each is listed in the design doc):
   * labels are formed per whole document before a row split, so the last token
@@ -18,7 +19,13 @@ Readings taken where the page is silent (each is listed in the design doc):
   * documents with no tokens are dropped before packing (they add no tokens, no
     segment, and do not count towards micro_bsz);
   * build_unpack's rows take the documents in order, micro_bsz per row, and its
-    cu_seqlens / indexes follow the same convention as build_pack's.
+    cu_seqlens / indexes follow the same convention as build_pack's;
+  * unpack_data keeps a row's first micro_bsz documents, each cut to seq_len
+    (both always hold for build_unpack rows; they only matter for carry-over
+    rows, which the page never unpacks);
+  * split_data_sequence_parallel cuts the last (sequence) dimension of every
+    row into tp equal contiguous slices, rank r taking slice r; the length
+    must be a multiple of tp.
 
 Pins: tests/test_oracle_pack.py (the page's printed examples, byte for byte,
 plus invariants on random inputs).
@@ -155,6 +162,26 @@ def unpack_data(row: Dict, micro_bsz: int, seq_len: int) -> Dict:
     ids = [[PAD_ID] * seq_len for _ in range(micro_bsz)]
     labels = [[IGNORE] * seq_len for _ in range(micro_bsz)]
     for i, (s, e) in enumerate(zip(starts, ends)):
+        if i >= micro_bsz:
+            break
+        e = min(e, s + seq_len)
         ids[i][: e - s] = row["input_ids"][s:e]
         labels[i][: e - s] = row["labels"][s:e]
     return {"input_ids": ids, "labels": labels}
+
+
+def split_sequence_parallel(rows: Sequence[Sequence[int]], tp: int, rank: int) -> List[List[int]]:
+    """Slice `rank` of the sequence dimension cut into `tp` equal parts
+    (section "处理数据", split_data_sequence_parallel)."""
+    out = []
+    for r in rows:
+        n = len(r)
+        assert n % tp == 0 and 0 <= rank < tp
+        w = n // tp
+        out.append(list(r[rank * w:(rank + 1) * w]))
+    return out
+
+
+def max_seqlen(cu_seqlens: Sequence[int]) -> int:
+    """packed_data_normalizer's max_seqlen: the longest segment of a row."""
+    return max(b - a for a, b in zip(cu_seqlens[:-1], cu_seqlens[1:]))

@@ -45,6 +45,48 @@ def test_unpack_data_page_example_pins_unpack_boundaries():
     assert un["labels"] == g["labels"]
 
 
+def test_normalizer_and_split_sp_page_examples():
+    # the first micro batch of the page's build_pack example after
+    # packed_data_normalizer, and both tp = 2 splits (packed and unpacked)
+    g = golden("p1_split_sp.json")
+    gp = golden("p1_build_pack.json")
+    row = pack_ref.build_pack(gp["docs"], gp["micro_bsz"], gp["seq_len"])[0]
+    pk = g["packed"]
+    assert row["input_ids"] == pk["input_ids"]
+    assert row["labels"] == pk["label"]
+    assert row["indexes"] == pk["indexes"]
+    assert row["cu_seqlens"] == pk["cu_seqlens"]
+    assert pack_ref.max_seqlen(row["cu_seqlens"]) == pk["max_seqlen"] == row["max_seqlen"]
+    for r, want in enumerate(pk["ranks"]):
+        for key, src in (("input_ids", row["input_ids"]), ("indexes", row["indexes"]), ("label", row["labels"])):
+            assert pack_ref.split_sequence_parallel([src], g["tp"], r) == [want[key]], (r, key)
+    gu = golden("p1_unpack_data.json")
+    urow = pack_ref.build_unpack(gu["docs"], gu["micro_bsz"], gu["seq_len"])[0]
+    un = pack_ref.unpack_data(urow, gu["micro_bsz"], gu["seq_len"])
+    up = g["unpacked"]
+    assert un["input_ids"] == up["input_ids"] and un["labels"] == up["label"]
+    for r, want in enumerate(up["ranks"]):
+        assert pack_ref.split_sequence_parallel(un["input_ids"], g["tp"], r) == want["input_ids"]
+        assert pack_ref.split_sequence_parallel(un["labels"], g["tp"], r) == want["label"]
+
+
+@pytest.mark.parametrize("tp", [1, 2, 4, 8, 16])
+def test_split_sp_ranks_concatenate_back(tp):
+    rng = np.random.default_rng(tp)
+    rows = [list(rng.integers(-100, 50000, 32)) for _ in range(3)]
+    parts = [pack_ref.split_sequence_parallel(rows, tp, r) for r in range(tp)]
+    for i, row in enumerate(rows):
+        assert sum((p[i] for p in parts), []) == row
+
+
+def test_unpack_data_of_carry_over_rows_keeps_first_docs_cut():
+    # reading: at most micro_bsz documents, each cut to seq_len
+    row = pack_ref.build_pack([[1] * 3, [2] * 9, [3] * 2, [4] * 2], 2, 8)[0]  # segments 3, 9, 2, 2
+    un = pack_ref.unpack_data(row, 2, 8)
+    assert un["input_ids"] == [[1, 1, 1, 0, 0, 0, 0, 0], [2] * 8]
+    assert un["labels"][1] == [2] * 8  # the cut keeps the document's own next-token labels
+
+
 def _check_row_structure(row, PL):
     cu = row["cu_seqlens"]
     assert cu[0] == 0 and cu[-1] == PL
