@@ -182,6 +182,43 @@ def rope_rate(psc, torch, np, qd, kd, pk, w, args):
             "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "launches": launches}
 
 
+def data_steps_rate(psc, torch, np, pk, w):
+    """The data steps after the packer on this workload's packer output, timed
+    apart from the step: per-row max_seqlen, unpack_data with the workload's
+    micro_bsz / SEQ_LEN, and the tp = 8 split of input_ids, labels and indexes.
+    Algorithmic bytes: every int32 read and written once."""
+    mb, sl = w.pack.micro_bsz, w.pack.seq_len
+    rows, PL = pk["input_ids"].shape
+    tp = 8 if PL % 8 == 0 else 1
+
+    def once():
+        psc.row_max_seqlen(pk)
+        psc.unpack_data(pk, mb, sl)
+        for key in ("input_ids", "labels", "indexes"):
+            psc.split_sequence(pk[key], tp, tp - 1)
+
+    for _ in range(3):
+        once()
+    torch.cuda.synchronize()
+    psc.timing_reset()
+    psc.timing_enable(True)
+    n = 20
+    for _ in range(n):
+        once()
+    torch.cuda.synchronize()
+    psc.timing_enable(False)
+    ms_total, launches = psc.timing_read()["data_steps"]
+    ms = ms_total / n
+    nseg = pk["cu_seqlens"].numel()
+    nbytes = 4 * ((rows + 1) + nseg + rows)                       # row max_seqlen
+    nbytes += 4 * (2 * rows * PL + 2 * rows * mb * sl + nseg + 2 * rows)  # unpack_data (upper bound on reads)
+    nbytes += 3 * 4 * 2 * rows * (PL // tp)                       # three splits
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"kernels": "row_max_seqlen+unpack_data+split_sequence x3", "bound": "hbm", "ms": round(ms, 4),
+            "launches_per_call": launches // n, "bytes": nbytes, "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+            "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "tp": tp}
+
+
 def doc_sweep(args):
     """The Sample Packing page's document-length measurement (section 5.3) on
     this kernel: each layout of one 32768-token row with its document mask,
@@ -394,6 +431,7 @@ def main():
                          "tflops": round(bwd_flops / (bwd_ms * 1e-3) / 1e12, 2),
                          "pct_peak": round(100 * bwd_flops / (bwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2)}
     result["rope"] = rope_rate(psc, torch, np, qd, kd, pk, w, args)
+    result["data_steps"] = data_steps_rate(psc, torch, np, pk, w)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, q, k, v, do, cu_h, real, args.cpu_seconds)
     print(json.dumps(result), flush=True)

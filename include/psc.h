@@ -131,6 +131,43 @@ int psc_pack_build(int mode, const int32_t* tokens, const int64_t* doc_offsets,
                    size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ */
+/* Data steps after the packer                                                */
+/* ------------------------------------------------------------------------ */
+/*
+ * InternEvo "数据加载与流程", section "处理数据".  cu_seqlens, row_seg_ptr and
+ * row_valid_len are psc_pack_build's outputs (flattened cu_seqlens: row r's
+ * boundaries are cu_seqlens[row_seg_ptr[r] .. row_seg_ptr[r+1]], offset by
+ * r*packed_len); n_cu = number of entries of the cu_seqlens buffer
+ * (max_segments + 1).  Reads are clamped to each row, so inconsistent
+ * boundaries cannot address outside the buffers.  Errors: PSC_ERR_INVALID
+ * (null pointer with a nonzero size, negative or oversized sizes, tp or rank
+ * out of range, length not a multiple of tp), PSC_ERR_HIP.
+ */
+
+/* psc_row_max_seqlen — packed_data_normalizer's max_seqlen: out[r] = the
+ * longest segment of row r (padding tail included), int32 [n_rows]. */
+int psc_row_max_seqlen(const int32_t* cu_seqlens, int64_t n_cu, const int32_t* row_seg_ptr, int64_t n_rows,
+                       int32_t* out, void* stream);
+
+/* psc_unpack_data — unpack_data: document i < micro_bsz of packed row r
+ * (input_ids, labels [n_rows, packed_len]) goes to row r*micro_bsz + i of
+ * out_ids, out_labels [n_rows*micro_bsz, seq_len], cut to seq_len, padded
+ * with ids 0 and labels -100.  A segment starting at or past row_valid_len[r]
+ * is the padding tail, not a document; a row's documents past micro_bsz are
+ * dropped (only carry-over rows can have them). */
+int psc_unpack_data(const int32_t* input_ids, const int32_t* labels, int64_t n_rows, int32_t packed_len,
+                    const int32_t* cu_seqlens, int64_t n_cu, const int32_t* row_seg_ptr,
+                    const int32_t* row_valid_len, int32_t micro_bsz, int32_t seq_len, int32_t* out_ids,
+                    int32_t* out_labels, void* stream);
+
+/* psc_split_sequence — split_data_sequence_parallel of one int32 array
+ * [rows, length] (input_ids, labels or indexes; packed or unpacked): rank
+ * `rank` of `tp` gets out [rows, length/tp] = in[:, rank*length/tp ...).
+ * length must be a multiple of tp, 0 <= rank < tp. */
+int psc_split_sequence(const int32_t* in, int64_t rows, int32_t length, int32_t tp, int32_t rank, int32_t* out,
+                       void* stream);
+
+/* ------------------------------------------------------------------------ */
 /* Rotary position embedding from the packer's indexes                      */
 /* ------------------------------------------------------------------------ */
 
@@ -235,7 +272,8 @@ typedef enum psc_kernel {
   PSC_K_ATTN_BWD_PRE = 3,
   PSC_K_ATTN_BWD_DKDV = 4,
   PSC_K_ATTN_BWD_DQ = 5,
-  PSC_K_ROPE = 6
+  PSC_K_ROPE = 6,
+  PSC_K_DATA_STEPS = 7
 } psc_kernel;
 
 int psc_timing_enable(int enable);

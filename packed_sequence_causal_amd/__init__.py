@@ -57,6 +57,11 @@ _SIGNATURES = {
                                            ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32,
                                            ctypes.c_int32, ctypes.c_int32, ctypes.c_float, _vp, _vp, _vp, _vp,
                                            ctypes.c_size_t, _vp]),
+    "psc_row_max_seqlen": (ctypes.c_int, [_vp, ctypes.c_int64, _vp, ctypes.c_int64, _vp, _vp]),
+    "psc_unpack_data": (ctypes.c_int, [_vp, _vp, ctypes.c_int64, ctypes.c_int32, _vp, ctypes.c_int64, _vp, _vp,
+                                       ctypes.c_int32, ctypes.c_int32, _vp, _vp, _vp]),
+    "psc_split_sequence": (ctypes.c_int, [_vp, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _vp,
+                                          _vp]),
     "psc_rope": (ctypes.c_int, [ctypes.c_int, _vp, ctypes.c_int64, ctypes.c_int32, _vp, ctypes.c_int64,
                                 ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, _vp, ctypes.c_float, ctypes.c_int,
                                 _vp]),
@@ -234,6 +239,55 @@ def varlen_attn_bwd(q, k, v, out, dout, lse, cu_seqlens, max_seqlen: int, n_segm
 
 # ---------------------------------------------------------- instrumentation
 
+def row_max_seqlen(packed: dict, out=None, stream=None):
+    """packed_data_normalizer's max_seqlen of every row of pack_build's output
+    (int32 [n_rows])."""
+    import torch
+
+    n_rows = packed["row_seg_ptr"].numel() - 1
+    if out is None:
+        out = torch.empty(n_rows, dtype=torch.int32, device=packed["cu_seqlens"].device)
+    _check(lib().psc_row_max_seqlen(_ptr(packed["cu_seqlens"]), packed["cu_seqlens"].numel(),
+                                    _ptr(packed["row_seg_ptr"]), n_rows, _ptr(out), _stream(stream)),
+           "psc_row_max_seqlen")
+    return out
+
+
+def unpack_data(packed: dict, micro_bsz: int, seq_len: int, out_ids=None, out_labels=None, stream=None):
+    """unpack_data of pack_build's output: (input_ids, labels) int32
+    [n_rows * micro_bsz, seq_len], one document per row."""
+    import torch
+
+    ids = packed["input_ids"]
+    n_rows, PL = ids.shape
+    rvl = packed.get("row_valid_len")
+    if rvl is None:
+        raise ValueError("unpack_data needs the packer's row_valid_len")
+    i32 = dict(dtype=torch.int32, device=ids.device)
+    out_ids = torch.empty(n_rows * micro_bsz, seq_len, **i32) if out_ids is None else out_ids
+    out_labels = torch.empty(n_rows * micro_bsz, seq_len, **i32) if out_labels is None else out_labels
+    _check(lib().psc_unpack_data(_ptr(ids), _ptr(packed["labels"]), n_rows, PL, _ptr(packed["cu_seqlens"]),
+                                 packed["cu_seqlens"].numel(), _ptr(packed["row_seg_ptr"]), _ptr(rvl), micro_bsz,
+                                 seq_len, _ptr(out_ids), _ptr(out_labels), _stream(stream)), "psc_unpack_data")
+    return out_ids, out_labels
+
+
+def split_sequence(x, tp: int, rank: int, out=None, stream=None):
+    """split_data_sequence_parallel of an int32 [rows, length] tensor: rank
+    `rank` of `tp` gets [rows, length / tp]."""
+    import torch
+
+    if x.dim() != 2 or not x.is_contiguous() or x.dtype != torch.int32:
+        raise ValueError("x must be a contiguous int32 [rows, length] tensor")
+    rows, length = x.shape
+    if tp < 1 or length % tp:
+        raise ValueError("length must be a multiple of tp")
+    out = torch.empty(rows, length // tp, dtype=torch.int32, device=x.device) if out is None else out
+    _check(lib().psc_split_sequence(_ptr(x), rows, length, tp, rank, _ptr(out), _stream(stream)),
+           "psc_split_sequence")
+    return out
+
+
 def rope(q, k, positions, base: float = 10000.0, inverse: bool = False, stream=None):
     """Rotate q [T,hq,D] and k [T,hkv,D] (or None) in place by positions int32
     [T] (the packer's indexes); inverse=True applies the backward rotation.
@@ -251,7 +305,7 @@ def rope(q, k, positions, base: float = 10000.0, inverse: bool = False, stream=N
 
 
 KERNELS = {"pack": 0, "attn_schedule": 1, "attn_fwd": 2, "attn_bwd_pre": 3, "attn_bwd_dkdv": 4, "attn_bwd_dq": 5,
-           "rope": 6}
+           "rope": 6, "data_steps": 7}
 
 
 def timing_enable(on: bool = True):

@@ -266,4 +266,52 @@ int psc_rope(int dtype, void* q, int64_t q_tok_stride, int32_t hq, void* k, int6
   return e == hipSuccess ? PSC_OK : PSC_ERR_HIP;
 }
 
+int psc_row_max_seqlen(const int32_t* cu_seqlens, int64_t n_cu, const int32_t* row_seg_ptr, int64_t n_rows,
+                       int32_t* out, void* stream) {
+  if (n_rows < 0 || n_rows >= kI32Max || n_cu < 1 || n_cu > kI32Max) return PSC_ERR_INVALID;
+  if (n_rows == 0) return PSC_OK;
+  if (!cu_seqlens || !row_seg_ptr || !out) return PSC_ERR_INVALID;
+  const hipError_t e = psc::launch_row_max_seqlen(cu_seqlens, n_cu, row_seg_ptr, n_rows, out,
+                                                  static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PSC_OK : PSC_ERR_HIP;
+}
+
+int psc_unpack_data(const int32_t* input_ids, const int32_t* labels, int64_t n_rows, int32_t packed_len,
+                    const int32_t* cu_seqlens, int64_t n_cu, const int32_t* row_seg_ptr,
+                    const int32_t* row_valid_len, int32_t micro_bsz, int32_t seq_len, int32_t* out_ids,
+                    int32_t* out_labels, void* stream) {
+  if (n_rows < 0 || packed_len < 1 || micro_bsz < 1 || seq_len < 1 || n_cu < 1 || n_cu > kI32Max)
+    return PSC_ERR_INVALID;
+  if (n_rows * (int64_t)packed_len > kI32Max) return PSC_ERR_INVALID;
+  if (n_rows * (int64_t)micro_bsz * seq_len > (int64_t(1) << 40)) return PSC_ERR_INVALID;
+  if (n_rows == 0) return PSC_OK;
+  if (!input_ids || !labels || !cu_seqlens || !row_seg_ptr || !row_valid_len || !out_ids || !out_labels)
+    return PSC_ERR_INVALID;
+  psc::UnpackArgs a;
+  a.input_ids = input_ids;
+  a.labels = labels;
+  a.cu = cu_seqlens;
+  a.row_seg_ptr = row_seg_ptr;
+  a.row_valid_len = row_valid_len;
+  a.out_ids = out_ids;
+  a.out_labels = out_labels;
+  a.n_rows = n_rows;
+  a.n_cu = n_cu;
+  a.packed_len = packed_len;
+  a.micro_bsz = micro_bsz;
+  a.seq_len = seq_len;
+  const hipError_t e = psc::launch_unpack(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PSC_OK : PSC_ERR_HIP;
+}
+
+int psc_split_sequence(const int32_t* in, int64_t rows, int32_t length, int32_t tp, int32_t rank, int32_t* out,
+                       void* stream) {
+  if (rows < 0 || length < 0 || tp < 1 || rank < 0 || rank >= tp || length % tp != 0) return PSC_ERR_INVALID;
+  if (rows * (int64_t)length > (int64_t(1) << 40)) return PSC_ERR_INVALID;
+  if (rows == 0 || length == 0) return PSC_OK;
+  if (!in || !out) return PSC_ERR_INVALID;
+  const hipError_t e = psc::launch_split(in, rows, length, tp, rank, out, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PSC_OK : PSC_ERR_HIP;
+}
+
 }  // extern "C"

@@ -9,7 +9,7 @@
 namespace psc {
 
 // Kernel timing slots (numbering matches enum psc_kernel in psc.h).
-enum TimerSlot { kTimePack = 0, kTimeSchedule, kTimeFwd, kTimeBwdPre, kTimeBwdDkdv, kTimeBwdDq, kTimeRope, kTimerSlots };
+enum TimerSlot { kTimePack = 0, kTimeSchedule, kTimeFwd, kTimeBwdPre, kTimeBwdDkdv, kTimeBwdDq, kTimeRope, kTimeData, kTimerSlots };
 
 // Brackets the launches made during its lifetime with HIP events on `stream`
 // when timing is switched on (timing.hip); does nothing otherwise.
@@ -118,5 +118,19 @@ struct RopeArgs {
   double inv_freq[64];  // base^(-2i/D), i < D/2
 };
 hipError_t launch_rope(const RopeArgs& a, hipStream_t stream);
+
+// unpack_data of packed rows [n_rows, packed_len] with the packer's flattened
+// cu_seqlens (n_cu entries), row_seg_ptr and row_valid_len.
+struct UnpackArgs {
+  const int32_t *input_ids, *labels, *cu, *row_seg_ptr, *row_valid_len;
+  int32_t *out_ids, *out_labels;
+  int64_t n_rows, n_cu;
+  int32_t packed_len, micro_bsz, seq_len;
+};
+hipError_t launch_unpack(const UnpackArgs& a, hipStream_t stream);
+hipError_t launch_split(const int32_t* in, int64_t rows, int32_t length, int32_t tp, int32_t rank, int32_t* out,
+                        hipStream_t stream);
+hipError_t launch_row_max_seqlen(const int32_t* cu, int64_t n_cu, const int32_t* row_seg_ptr, int64_t n_rows,
+                                 int32_t* out, hipStream_t stream);
 
 }  // namespace psc

@@ -111,7 +111,7 @@ int psc_timing_read(int kernel, double* total_ms, int64_t* launches) {
 
 const char* psc_kernel_name(int kernel) {
   static const char* names[psc::kTimerSlots] = {"pack",          "attn_schedule", "attn_fwd", "attn_bwd_pre",
-                                                "attn_bwd_dkdv", "attn_bwd_dq",   "rope"};
+                                                "attn_bwd_dkdv", "attn_bwd_dq",   "rope",     "data_steps"};
   return (kernel >= 0 && kernel < psc::kTimerSlots) ? names[kernel] : "unknown";
 }
 

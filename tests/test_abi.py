@@ -179,3 +179,43 @@ def test_rope_empty_is_a_no_op():
     assert _rope_raw(T=0, q=None, k=None, pos=None) == 0
     assert _rope_raw(T=0) == 0
 
+
+
+def _vp(x):
+    return None if x is None else ctypes.c_void_p(x)
+
+
+def _unpack_raw(**kw):
+    a = dict(ids=16, labels=16, n_rows=2, PL=16, cu=16, n_cu=8, rsp=16, rvl=16, mb=2, sl=8, oi=16, ol=16)
+    a.update(kw)
+    return psc.lib().psc_unpack_data(_vp(a["ids"]), _vp(a["labels"]), a["n_rows"], a["PL"], _vp(a["cu"]), a["n_cu"],
+                                     _vp(a["rsp"]), _vp(a["rvl"]), a["mb"], a["sl"], _vp(a["oi"]), _vp(a["ol"]),
+                                     None)
+
+
+@pytest.mark.parametrize("kw", [dict(n_rows=-1), dict(PL=0), dict(mb=0), dict(sl=0), dict(n_cu=0),
+                                dict(ids=None), dict(rvl=None), dict(oi=None), dict(cu=None),
+                                dict(n_rows=1 << 20, PL=1 << 12)])
+def test_unpack_data_rejects_on_host(kw):
+    assert _unpack_raw(**kw) == psc.ERR_INVALID
+
+
+def test_unpack_data_no_rows_is_a_no_op():
+    assert _unpack_raw(n_rows=0, ids=None, labels=None, cu=None, rsp=None, rvl=None, oi=None, ol=None) == 0
+
+
+@pytest.mark.parametrize("args", [(16, -1, 16, 2, 0, 16), (16, 2, 16, 0, 0, 16), (16, 2, 16, 2, 2, 16),
+                                  (16, 2, 16, 2, -1, 16), (16, 2, 15, 2, 0, 16), (None, 2, 16, 2, 0, 16),
+                                  (16, 2, 16, 2, 0, None)])
+def test_split_sequence_rejects_on_host(args):
+    i, rows, length, tp, rank, o = args
+    assert psc.lib().psc_split_sequence(_vp(i), rows, length, tp, rank, _vp(o), None) == psc.ERR_INVALID
+
+
+def test_split_and_row_max_no_ops():
+    L = psc.lib()
+    assert L.psc_split_sequence(None, 0, 16, 4, 1, None, None) == 0
+    assert L.psc_row_max_seqlen(None, 1, None, 0, None, None) == 0
+    assert L.psc_row_max_seqlen(None, 0, None, 0, None, None) == psc.ERR_INVALID
+    assert L.psc_row_max_seqlen(_vp(16), 4, _vp(16), 2, None, None) == psc.ERR_INVALID
+    assert L.psc_row_max_seqlen(_vp(16), 4, _vp(16), -1, _vp(16), None) == psc.ERR_INVALID
