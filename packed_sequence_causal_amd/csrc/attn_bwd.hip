@@ -160,10 +160,13 @@ __global__ void __launch_bounds__(kThreads, 2) k_bwd_dq(BwdParams p) {
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const uint32_t b = xcd_group_remap(blockIdx.x, gridDim.x, (uint32_t)p.group);
   const uint32_t item = b / (uint32_t)p.hq, head = b % (uint32_t)p.hq;
+  // item < cap (the grid is cap work-groups per head), so the entry is read
+  // together with the count and used only once the count admits it.  Segment
+  // bounds come clamped to [0, T] from the schedule: a malformed cu_seqlens
+  // cannot send any access outside the tensors.
+  const int4 it = *reinterpret_cast<const int4*>(p.items + 4 * item);
   if ((int32_t)item >= *p.n_items) return;
-  const int32_t seg = p.items[2 * item], tile = p.items[2 * item + 1];
-  const int32_t s0 = min(max(p.cu[seg], 0), (int32_t)p.T);
-  const int32_t L = min(max(p.cu[seg + 1], s0), (int32_t)p.T) - s0;
+  const int32_t s0 = it.x, L = it.y, tile = it.z;
   const int32_t q0 = tile * kBQ;
   if (q0 >= L) return;
   const int32_t kvh = (int32_t)head / p.group;
@@ -490,10 +493,13 @@ __global__ void __launch_bounds__(kThreads, 1) k_bwd_dkdv(BwdParams p) {
 
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, h = l >> 5, lq = l & 31;
   const uint32_t item = blockIdx.x / (uint32_t)p.hkv, kvh = blockIdx.x % (uint32_t)p.hkv;
+  // item < cap (the grid is cap work-groups per head), so the entry is read
+  // together with the count and used only once the count admits it.  Segment
+  // bounds come clamped to [0, T] from the schedule: a malformed cu_seqlens
+  // cannot send any access outside the tensors.
+  const int4 it = *reinterpret_cast<const int4*>(p.items + 4 * item);
   if ((int32_t)item >= *p.n_items) return;
-  const int32_t seg = p.items[2 * item], tile = p.items[2 * item + 1];
-  const int32_t s0 = min(max(p.cu[seg], 0), (int32_t)p.T);
-  const int32_t L = min(max(p.cu[seg + 1], s0), (int32_t)p.T) - s0;
+  const int32_t s0 = it.x, L = it.y, tile = it.z;
   const int32_t kb = tile * kBKV;
   if (kb >= L) return;
   const int32_t key = kb + 32 * w + lq;  // this lane's key (S layout: lane <-> key)

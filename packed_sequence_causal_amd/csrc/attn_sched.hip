@@ -134,8 +134,10 @@ __global__ void __launch_bounds__(kThreads) k_sched_fill(const int32_t* cu, int3
   tile_of(toff, n_seg, i, s, t);
   const int32_t pos = atomicAdd(&hist[tile_bin(cu, s, t, T, tile, unit, suffix, n_bins)], 1);
   if (pos < cap) {
-    items[2 * pos] = s;
-    items[2 * pos + 1] = t;
+    // the segment's clamped start and length travel with the item, so a
+    // consumer needs one load (not item, then cu_seqlens) before its operands
+    const int32_t a = min(max(cu[s], 0), T);
+    *reinterpret_cast<int4*>(items + 4 * pos) = make_int4(a, seg_len(cu, s, T), t, s);
   }
 }
 
@@ -147,7 +149,7 @@ static int64_t sched_cap(int64_t T, int32_t n_seg, int tile) { return T / tile +
 static int32_t sched_bins(int32_t max_seqlen, int unit) { return (max_seqlen + unit - 1) / unit + 2; }
 
 size_t schedule_bytes(int64_t T, int32_t n_seg, int32_t max_seqlen, int tile, int unit) {
-  return align_up(sizeof(int32_t) * 2 * sched_cap(T, n_seg, tile), 256) +
+  return align_up(sizeof(int32_t) * 4 * sched_cap(T, n_seg, tile), 256) +
          align_up(sizeof(int32_t) * sched_bins(max_seqlen, unit), 256) +
          align_up(sizeof(int32_t) * ((size_t)n_seg + 1), 256) + 256;
 }
@@ -158,7 +160,7 @@ TileSchedule schedule_carve(void* ws, int64_t T, int32_t n_seg, int32_t max_seql
   s.cap = sched_cap(T, n_seg, tile);
   s.n_bins = sched_bins(max_seqlen, unit);
   s.items = reinterpret_cast<int32_t*>(p);
-  p += align_up(sizeof(int32_t) * 2 * s.cap, 256);
+  p += align_up(sizeof(int32_t) * 4 * s.cap, 256);
   s.hist = reinterpret_cast<int32_t*>(p);
   p += align_up(sizeof(int32_t) * s.n_bins, 256);
   s.toff = reinterpret_cast<int32_t*>(p);

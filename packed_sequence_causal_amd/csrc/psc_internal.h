@@ -86,7 +86,7 @@ struct AttnBwdArgs {
 
 // Work list of (segment, tile) pairs, most work first (attn_sched.hip).
 struct TileSchedule {
-  int32_t* items;     // [2 * cap]: segment, tile index inside the segment
+  int32_t* items;     // [4 * cap]: segment start, segment length, tile index, segment
   int32_t* hist;      // [n_bins]: tiles per work bin, then scatter cursors
   int32_t* toff;      // [n_seg + 1]: first tile of each segment (scan of tile counts)
   int32_t* n_items;   // [1]: tiles actually listed
