@@ -269,7 +269,7 @@ typedef enum psc_kernel {
   PSC_K_PACK = 0,
   PSC_K_ATTN_SCHEDULE = 1,
   PSC_K_ATTN_FWD = 2,
-  PSC_K_ATTN_BWD_PRE = 3,
+  PSC_K_ATTN_BWD_PRE = 3, /* reserved: not launched any more (the dQ kernel computes D) */
   PSC_K_ATTN_BWD_DKDV = 4,
   PSC_K_ATTN_BWD_DQ = 5,
   PSC_K_ROPE = 6,

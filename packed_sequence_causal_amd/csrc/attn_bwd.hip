@@ -2,7 +2,9 @@
 //
 // Gradients of sum(dO * O) for O = softmax(scale * Q K^T restricted to each
 // document's causal triangle) V, with P recomputed from the forward's lse:
-//   D_i   = <dO_i, O_i>                      (k_bwd_pre, with lse_i * log2 e)
+//   D_i   = <dO_i, O_i>                      (in k_bwd_dq, stored with lse_i *
+//                                              log2 e for k_bwd_dkdv, which
+//                                              runs after it)
 //   P     = exp(scale * q_i.k_j - lse_i)      (recomputed, exp2 domain)
 //   dP    = dO V^T,   dS = P * (dP - D)
 //   dV    = P^T dO,   dK = scale dS^T Q       (k_bwd_dkdv: one workgroup per
@@ -48,42 +50,6 @@ struct BwdParams {
   int32_t hq, hkv, group;
   float scale, scale_log2;
 };
-
-// D[h][t] = sum_d dO[t,h,d] * O[t,h,d] and L2[h][t] = lse[h][t] * log2(e).
-// One workgroup = 64 tokens of one head; D/8 lanes read one row (coalesced),
-// the 64 results are written as one contiguous run.
-template <int D>
-__global__ void __launch_bounds__(kThreads) k_bwd_pre(BwdParams p) {
-  constexpr int LPR = D / 8;             // lanes per row
-  constexpr int RPP = kThreads / LPR;    // rows per pass
-  __shared__ float res[64];
-  const int h = blockIdx.y;
-  const int64_t t0 = (int64_t)blockIdx.x * 64;
-  const int part = threadIdx.x % LPR;
-#pragma unroll
-  for (int pass = 0; pass < 64 / RPP; ++pass) {
-    const int r = pass * RPP + threadIdx.x / LPR;
-    const int64_t t = t0 + r;
-    float acc = 0.f;
-    if (t < p.T) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(p.o + t * p.so + (int64_t)h * D + part * 8);
-      const bf16x8 b = *reinterpret_cast<const bf16x8*>(p.dout + t * p.sdo + (int64_t)h * D + part * 8);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc = __builtin_fmaf((float)a[e], (float)b[e], acc);
-    }
-#pragma unroll
-    for (int o = LPR / 2; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
-    if (part == 0) res[r] = acc;
-  }
-  __syncthreads();
-  if (threadIdx.x < 64) {
-    const int64_t t = t0 + threadIdx.x;
-    if (t < p.T) {
-      p.Dbuf[(int64_t)h * p.T + t] = res[threadIdx.x];
-      p.L2buf[(int64_t)h * p.T + t] = p.lse[(int64_t)h * p.T + t] * kLog2e;
-    }
-  }
-}
 
 // ---------------------------------------------------------------------- dQ
 
@@ -193,8 +159,28 @@ __global__ void __launch_bounds__(kThreads, 2) k_bwd_dq(BwdParams p) {
       st.df[kk] = qvalid ? *reinterpret_cast<const bf16x8*>(Dr + 16 * kk + 8 * h) : bf16x8{};
     }
   }
-  st.lse2 = qvalid ? p.L2buf[(int64_t)head * p.T + s0 + qrow] : 0.f;
-  st.Drow = qvalid ? p.Dbuf[(int64_t)head * p.T + s0 + qrow] : 0.f;
+  // D_i = <dO_i, O_i> from the dO fragments already held (lanes l and l ^ 32
+  // hold the two halves of row lq) and the same fragments of O; D and
+  // lse * log2 e are also stored for the dK/dV kernel, which runs next.  The
+  // tiles partition every document, so each (row, head) is written once.
+  {
+    float dacc = 0.f;
+    if (qvalid) {
+      const bf16* Or = p.o + (int64_t)(s0 + qrow) * p.so + (int64_t)head * D;
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk) {
+        const bf16x8 of = *reinterpret_cast<const bf16x8*>(Or + 16 * kk + 8 * h);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) dacc = __builtin_fmaf((float)of[e], (float)st.df[kk][e], dacc);
+      }
+    }
+    st.Drow = sum_halves(dacc);
+    st.lse2 = qvalid ? p.lse[(int64_t)head * p.T + s0 + qrow] * kLog2e : 0.f;
+    if (qvalid && h == 0) {
+      p.Dbuf[(int64_t)head * p.T + s0 + qrow] = st.Drow;
+      p.L2buf[(int64_t)head * p.T + s0 + qrow] = st.lse2;
+    }
+  }
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) st.acc[dt] = f32x16{};
 
@@ -626,29 +612,8 @@ hipError_t launch_attn_bwd_bf16(const AttnBwdArgs& a, hipStream_t stream) {
   p.scale_log2 = d.scale * kLog2e;
   if (d.T == 0) return hipSuccess;
 
-  {
-    ScopedKernelTimer timed(kTimeBwdPre, stream);
-    dim3 grid((unsigned)((d.T + 63) / 64), (unsigned)d.hq);
-    if (d.d == 128)
-      k_bwd_pre<128><<<grid, kThreads, 0, stream>>>(p);
-    else
-      k_bwd_pre<64><<<grid, kThreads, 0, stream>>>(p);
-  }
-
-  hipError_t e = launch_schedule(a.cu, d.n_seg, (int32_t)d.T, kBKV, kBMk, true, sk, stream);
-  if (e != hipSuccess) return e;
-  p.items = sk.items;
-  p.n_items = sk.n_items;
-  const unsigned grid_kv = (unsigned)(sk.cap * d.hkv);
-  {
-    ScopedKernelTimer timed(kTimeBwdDkdv, stream);
-    if (d.d == 128)
-      k_bwd_dkdv<128><<<grid_kv, kThreads, 0, stream>>>(p);
-    else
-      k_bwd_dkdv<64><<<grid_kv, kThreads, 0, stream>>>(p);
-  }
-
-  e = launch_schedule(a.cu, d.n_seg, (int32_t)d.T, kBQ, kBNq, false, sq, stream);
+  // dQ first: it also produces D and lse * log2 e, which dK/dV reads.
+  hipError_t e = launch_schedule(a.cu, d.n_seg, (int32_t)d.T, kBQ, kBNq, false, sq, stream);
   if (e != hipSuccess) return e;
   p.items = sq.items;
   p.n_items = sq.n_items;
@@ -659,6 +624,19 @@ hipError_t launch_attn_bwd_bf16(const AttnBwdArgs& a, hipStream_t stream) {
       k_bwd_dq<128><<<grid_q, kThreads, 0, stream>>>(p);
     else
       k_bwd_dq<64><<<grid_q, kThreads, 0, stream>>>(p);
+  }
+
+  e = launch_schedule(a.cu, d.n_seg, (int32_t)d.T, kBKV, kBMk, true, sk, stream);
+  if (e != hipSuccess) return e;
+  p.items = sk.items;
+  p.n_items = sk.n_items;
+  const unsigned grid_kv = (unsigned)(sk.cap * d.hkv);
+  {
+    ScopedKernelTimer timed(kTimeBwdDkdv, stream);
+    if (d.d == 128)
+      k_bwd_dkdv<128><<<grid_kv, kThreads, 0, stream>>>(p);
+    else
+      k_bwd_dkdv<64><<<grid_kv, kThreads, 0, stream>>>(p);
   }
   return hipGetLastError();
 }

@@ -9,6 +9,7 @@
 namespace psc {
 
 // Kernel timing slots (numbering matches enum psc_kernel in psc.h).
+// kTimeBwdPre is kept for stable ids; nothing is timed in it.
 enum TimerSlot { kTimePack = 0, kTimeSchedule, kTimeFwd, kTimeBwdPre, kTimeBwdDkdv, kTimeBwdDq, kTimeRope, kTimeData, kTimerSlots };
 
 // Brackets the launches made during its lifetime with HIP events on `stream`
