@@ -45,9 +45,9 @@ KERNEL_SOURCES = {
 }
 MEASURED_TRAFFIC = {
     # (kernel, workload): (sources sha256 prefix, read bytes, write bytes)
-    ("attn_fwd", "lognormal_32k"): ("0e9143c4ed062ec3", 2.0 * 1380831.0 * 1024, 533027.0 * 1024),
-    ("attn_bwd_dkdv", "lognormal_32k"): ("fb6e14feab08c92c", 2.0 * 4252791.0 * 1024, 524288.0 * 1024),
-    ("attn_bwd_dq", "lognormal_32k"): ("fb6e14feab08c92c", 2.0 * 1624388.8 * 1024, 1055073.9 * 1024),
+    ("attn_fwd", "lognormal_32k"): ("b3bacdc59a71e233", 2.0 * 1374493.0 * 1024, 533045.7 * 1024),
+    ("attn_bwd_dkdv", "lognormal_32k"): ("c6650b8699c7464e", 2.0 * 4170252.7 * 1024, 524288.0 * 1024),
+    ("attn_bwd_dq", "lognormal_32k"): ("c6650b8699c7464e", 2.0 * 1891521.2 * 1024, 1070681.0 * 1024),
 }
 
 

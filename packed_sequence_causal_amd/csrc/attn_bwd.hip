@@ -497,10 +497,13 @@ __global__ void __launch_bounds__(kThreads, 1) k_bwd_dkdv(BwdParams p) {
   uint32_t qoff[D / 8 / (kThreads / 64)], ooff[D / 8 / (kThreads / 64)];
   tile_offsets<D, kThreads / 64>(p.sq, w, l, qoff);
   tile_offsets<D, kThreads / 64>(p.sdo, w, l, ooff);
-  // iteration t: query head kvh*G + t / nqb, query block kb + (t % nqb) * 64
+  // iteration t: query head kvh*G + t / nqb, query block kb + (nqb - 1 - t % nqb) * 64.
+  // Blocks run from the document end back to the tile: every tile of a
+  // document starts at the same rows, so tiles of one document that run at
+  // the same time read the same Q/dO blocks together and L2 serves the rest.
   auto issue = [&](int32_t t, char* Qs, char* dOs, float* l2s, float* Ds) {
     const int32_t head = kvh * p.group + t / nqb;
-    const int32_t qs = kb + (t % nqb) * kBMk;
+    const int32_t qs = kb + (nqb - 1 - t % nqb) * kBMk;
     load_tile<D, kThreads / 64>(p.q + (int64_t)s0 * p.sq + (int64_t)head * D, p.sq, qs, L, qoff, Qs, w, l);
     load_tile<D, kThreads / 64>(p.dout + (int64_t)s0 * p.sdo + (int64_t)head * D, p.sdo, qs, L, ooff, dOs, w, l);
     if (w == 0) load_vec64_async(p.L2buf + (int64_t)head * p.T + s0, qs, L, l2s, l);
@@ -530,7 +533,7 @@ __global__ void __launch_bounds__(kThreads, 1) k_bwd_dkdv(BwdParams p) {
     __syncthreads();
     if (t + 1 < niter) issue(t + 1, Qs1, dOs1, l2s1, Ds1);
     {
-      const int32_t qs = kb + (t % nqb) * kBMk;
+      const int32_t qs = kb + (nqb - 1 - t % nqb) * kBMk;
       if (qs >= wk_lo + 31 && qs + kBMk <= L)
         dkdv_block_full<D>(st, Qs0, dOs0, l2s0, Ds0, c2, h, lq, l);
       else if (qs + kBMk - 1 >= wk_lo)
@@ -541,7 +544,7 @@ __global__ void __launch_bounds__(kThreads, 1) k_bwd_dkdv(BwdParams p) {
     __syncthreads();
     if (t + 2 < niter) issue(t + 2, Qs0, dOs0, l2s0, Ds0);
     {
-      const int32_t qs = kb + ((t + 1) % nqb) * kBMk;
+      const int32_t qs = kb + (nqb - 1 - (t + 1) % nqb) * kBMk;
       if (qs >= wk_lo + 31 && qs + kBMk <= L)
         dkdv_block_full<D>(st, Qs1, dOs1, l2s1, Ds1, c2, h, lq, l);
       else if (qs + kBMk - 1 >= wk_lo)
