@@ -141,6 +141,88 @@ __global__ void __launch_bounds__(kThreads) k_sched_fill(const int32_t* cu, int3
   }
 }
 
+// The whole schedule in one workgroup, for the common sizes (segments, bins
+// and tiles few enough for LDS and one block's loops): the same four stages
+// with the per-segment offsets and the bins in LDS, so one launch replaces
+// four.
+constexpr int kSmallThreads = 1024;
+constexpr int kSmallSeg = 4096;     // n_seg + 1 limit (toff in LDS)
+constexpr int kSmallBins = 4096;    // n_bins limit (histogram in LDS)
+constexpr int64_t kSmallCap = 131072;
+
+// Exclusive scan of v over the block (kSmallThreads lanes); returns this
+// lane's prefix and the block total through `tot`.
+__device__ inline int32_t block_exscan(int32_t v, int32_t* wsum, int32_t& tot) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  int32_t x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int32_t y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) wsum[wid] = x;
+  __syncthreads();
+  int32_t off = 0;
+  tot = 0;
+  for (int k = 0; k < kSmallThreads / 64; ++k) {
+    if (k < wid) off += wsum[k];
+    tot += wsum[k];
+  }
+  __syncthreads();
+  return off + x - v;
+}
+
+__global__ void __launch_bounds__(kSmallThreads) k_sched_small(const int32_t* cu, int32_t n_seg, int32_t T,
+                                                               int32_t tile, int32_t unit, bool suffix,
+                                                               int32_t n_bins, int32_t* items, int64_t cap,
+                                                               int32_t* n_items) {
+  __shared__ int32_t toff[kSmallSeg];
+  __shared__ int32_t hist[kSmallBins];
+  __shared__ int32_t wsum[kSmallThreads / 64];
+  for (int32_t i = threadIdx.x; i < n_bins; i += kSmallThreads) hist[i] = 0;
+  // tiles per segment, scanned into toff[0..n_seg]
+  int32_t carry = 0;
+  for (int32_t c = 0; c < n_seg; c += kSmallThreads) {
+    const int32_t sg = c + threadIdx.x;
+    const int32_t v = sg < n_seg ? (seg_len(cu, sg, T) + tile - 1) / tile : 0;
+    int32_t tot;
+    const int32_t ex = block_exscan(v, wsum, tot);
+    if (sg < n_seg) toff[sg] = carry + ex;
+    carry += tot;
+  }
+  if (threadIdx.x == 0) toff[n_seg] = carry;
+  __syncthreads();
+  const int32_t n = (int32_t)min((int64_t)carry, cap);
+  // histogram of work bins
+  for (int32_t i = threadIdx.x; i < n; i += kSmallThreads) {
+    int32_t sg, t;
+    tile_of(toff, n_seg, i, sg, t);
+    atomicAdd(&hist[tile_bin(cu, sg, t, T, tile, unit, suffix, n_bins)], 1);
+  }
+  __syncthreads();
+  // descending exclusive scan: cursor[b] = tiles in bins above b
+  carry = 0;
+  for (int32_t c = 0; c < n_bins; c += kSmallThreads) {
+    const int32_t i = c + threadIdx.x;
+    const int32_t b = n_bins - 1 - i;
+    const int32_t v = i < n_bins ? hist[b] : 0;
+    int32_t tot;
+    const int32_t ex = block_exscan(v, wsum, tot);
+    if (i < n_bins) hist[b] = carry + ex;
+    carry += tot;
+  }
+  __syncthreads();
+  // scatter: each tile takes the next slot of its bin
+  for (int32_t i = threadIdx.x; i < n; i += kSmallThreads) {
+    int32_t sg, t;
+    tile_of(toff, n_seg, i, sg, t);
+    const int32_t pos = atomicAdd(&hist[tile_bin(cu, sg, t, T, tile, unit, suffix, n_bins)], 1);
+    const int32_t a = min(max(cu[sg], 0), T);
+    *reinterpret_cast<int4*>(items + 4 * pos) = make_int4(a, seg_len(cu, sg, T), t, sg);
+  }
+  if (threadIdx.x == 0) *n_items = n;
+}
+
 }  // namespace
 
 // Upper bound on the number of tiles: sum over segments of ceil(L / tile)
@@ -172,6 +254,11 @@ TileSchedule schedule_carve(void* ws, int64_t T, int32_t n_seg, int32_t max_seql
 hipError_t launch_schedule(const int32_t* cu, int32_t n_seg, int32_t T, int tile, int unit, bool suffix,
                            const TileSchedule& s, hipStream_t stream) {
   ScopedKernelTimer timed(kTimeSchedule, stream);
+  if (n_seg + 1 <= kSmallSeg && s.n_bins <= kSmallBins && s.cap <= kSmallCap) {
+    k_sched_small<<<1, kSmallThreads, 0, stream>>>(cu, n_seg, T, tile, unit, suffix, s.n_bins, s.items, s.cap,
+                                                   s.n_items);
+    return hipGetLastError();
+  }
   const unsigned gt = (unsigned)((s.cap + kThreads - 1) / kThreads);
   k_sched_tiles<<<1, kThreads, 0, stream>>>(cu, n_seg, T, tile, s.toff, s.hist, s.n_bins, s.n_items);
   k_sched_count<<<gt, kThreads, 0, stream>>>(cu, n_seg, T, tile, unit, suffix, s.toff, s.hist, s.n_bins, s.cap);

@@ -131,6 +131,17 @@ def test_bf16_single_long_document_and_one_token_rows():
         full_compare(q, k, v, do, cu, "bf16")
 
 
+def test_bf16_many_tiny_documents_large_schedule_path():
+    # more than 4095 segments: the tile schedule is built by its multi-kernel
+    # path instead of the one-workgroup kernel used for common sizes
+    rng = np.random.default_rng(91)
+    lens = rng.integers(1, 9, 4600)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    T = int(cu[-1])
+    q, k, v, do = workloads.qkv_do(T, 2, 1, 64, seed=91, dtype="bf16")
+    full_compare(q, k, v, do, cu, "bf16")
+
+
 def test_bf16_packed_kv_views_match_contiguous():
     # kv stacked as [T, 2, Hkv, D]: k = kv[:, 0], v = kv[:, 1] (token stride 2*Hkv*D)
     cu = np.array([0, 100, 333, 700], dtype=np.int32)
