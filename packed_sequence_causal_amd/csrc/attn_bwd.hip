@@ -204,16 +204,39 @@ __global__ void __launch_bounds__(kThreads, 2) k_bwd_dq(BwdParams p) {
     if ((j + 1) * kBNq <= wq_hi) dq_block<D>(st, Ks1, Vs1, (j + 1) * kBNq, L, qrow, wq_lo, c2, h, lq, l);
   }
 
-  if (qvalid) {
-    float* Qd = p.dq + ((int64_t)(s0 + qrow) * p.hq + head) * D;
+  // Epilogue: dQ goes out through LDS so that each store instruction writes
+  // whole runs of 64 lanes x 16 bytes (4 rows) instead of 32-byte pieces of
+  // 32 rows.  The stage the last block did not use is free (its block was
+  // consumed before the last barrier, and no load targets it); each wave
+  // stages its 32 rows in its own half of one of its tiles, kPW columns at a
+  // time.  Inside a staged row, 16-byte chunk c sits at slot c ^ (row % kPC).
+  {
+    constexpr int kPW = tile_bytes<D>() / 256;  // fp32 columns per pass: 32 rows x kPW x 4 B = half a tile
+    constexpr int kPC = kPW / 4;                 // 16-byte chunks per staged row
+    char* stage = (nkv & 1) ? (w < 2 ? Ks1 : Vs1) : (w < 2 ? Ks0 : Vs0);
+    char* ob = stage + (w & 1) * (tile_bytes<D>() / 2);
 #pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt) {
+    for (int pass = 0; pass < D / kPW; ++pass) {
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        f32x4 v4;
+      for (int dt = 0; dt < D / 32; ++dt) {
+        if ((32 * dt) / kPW != pass) continue;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v4[e] = st.acc[dt][4 * g4 + e] * p.scale;
-        *reinterpret_cast<f32x4*>(Qd + 32 * dt + 8 * g4 + 4 * h) = v4;
+        for (int g4 = 0; g4 < 4; ++g4) {
+          f32x4 v4;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v4[e] = st.acc[dt][4 * g4 + e] * p.scale;
+          const int c = (32 * dt - kPW * pass) / 4 + 2 * g4 + h;
+          *reinterpret_cast<f32x4*>(ob + lq * (4 * kPW) + ((c ^ (lq & (kPC - 1))) << 4)) = v4;
+        }
+      }
+      constexpr int kRowsPerStore = 64 / kPC;
+      const int c = l % kPC;
+#pragma unroll
+      for (int k = 0; k < 32 / kRowsPerStore; ++k) {
+        const int r = k * kRowsPerStore + l / kPC;
+        const f32x4 v4 = *reinterpret_cast<const f32x4*>(ob + r * (4 * kPW) + ((c ^ (r & (kPC - 1))) << 4));
+        const int32_t row = wq_lo + r;
+        if (row < L) *reinterpret_cast<f32x4*>(p.dq + ((int64_t)(s0 + row) * p.hq + head) * D + kPW * pass + 4 * c) = v4;
       }
     }
   }

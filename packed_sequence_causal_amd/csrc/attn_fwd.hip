@@ -187,10 +187,18 @@ __global__ void __launch_bounds__(kThreads, 2) k_attn_fwd(FwdParams p) {
     if ((j + 1) * kBN <= wq_hi) fwd_block<D>(st, Ks1, Vs1, (j + 1) * kBN, L, qrow, wq_lo, c2, h, lq, l);
   }
 
+  // Epilogue.  O goes out through LDS so that each store instruction writes
+  // whole 2*D-byte rows (64 lanes x 16 bytes) instead of 16-byte pieces of
+  // 32 rows: the stage the last block did not use is free (its block was
+  // consumed before the last barrier, and no load targets it), and each wave
+  // stages its 32 rows in its own half of one of its two tiles.  Inside a
+  // row, 16-byte chunk c sits at slot c ^ (row % (D/8)).
   const float lt = sum_halves(st.l_i);
-  if (qvalid) {
-    const float inv = 1.f / lt;
-    bf16* Op = p.out + (int64_t)(s0 + qrow) * p.so + (int64_t)head * D;
+  const float inv = qvalid ? 1.f / lt : 0.f;
+  {
+    constexpr int kChunks = D / 8;
+    char* stage = (nkv & 1) ? (w < 2 ? Ks1 : Vs1) : (w < 2 ? Ks0 : Vs0);
+    char* ob = stage + (w & 1) * (tile_bytes<D>() / 2);
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt) {
 #pragma unroll
@@ -198,11 +206,21 @@ __global__ void __launch_bounds__(kThreads, 2) k_attn_fwd(FwdParams p) {
         bf16x4 o4;
 #pragma unroll
         for (int e = 0; e < 4; ++e) o4[e] = (bf16)(st.oacc[dt][4 * g4 + e] * inv);
-        *reinterpret_cast<bf16x4*>(Op + 32 * dt + 8 * g4 + 4 * h) = o4;
+        const int c = 4 * dt + g4;
+        *reinterpret_cast<bf16x4*>(ob + lq * (2 * D) + ((c ^ (lq & (kChunks - 1))) << 4) + 8 * h) = o4;
       }
     }
-    if (h == 0) p.lse[(int64_t)head * p.T + s0 + qrow] = (st.m_i + __log2f(lt)) * kLn2;
+    constexpr int kRowsPerStore = 64 / kChunks;
+    const int c = l % kChunks;
+#pragma unroll
+    for (int k = 0; k < 32 / kRowsPerStore; ++k) {
+      const int r = k * kRowsPerStore + l / kChunks;
+      const bf16x8 v8 = *reinterpret_cast<const bf16x8*>(ob + r * (2 * D) + ((c ^ (r & (kChunks - 1))) << 4));
+      const int32_t row = wq_lo + r;
+      if (row < L) *reinterpret_cast<bf16x8*>(p.out + (int64_t)(s0 + row) * p.so + (int64_t)head * D + 8 * c) = v8;
+    }
   }
+  if (qvalid && h == 0) p.lse[(int64_t)head * p.T + s0 + qrow] = (st.m_i + __log2f(lt)) * kLn2;
 }
 
 }  // namespace
