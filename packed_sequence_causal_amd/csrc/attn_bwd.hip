@@ -389,11 +389,12 @@ __device__ __forceinline__ void dkdv_block_full(DkvState<D>& st, const char* Qs,
       nq[kk] = ld8(Qs + offA(1, kk));
       nd[kk] = ld8(dOs + offA(1, kk));
     }
-    PSC_SCHED_DS_READ(4);
+    // eight operand reads ahead of the first MFMA, then one per MFMA
+    PSC_SCHED_DS_READ(8);
 #pragma unroll
     for (int i = 0; i < 2 * KS; ++i) {
       PSC_SCHED_MFMA(1);
-      PSC_SCHED_DS_READ(1);
+      if (i < 2 * KS - 4) PSC_SCHED_DS_READ(1);
     }
     PSC_SCHED_DS_READ(8 + 2 * PF);
   }
