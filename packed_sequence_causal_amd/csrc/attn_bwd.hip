@@ -100,6 +100,8 @@ __device__ __forceinline__ void dq_block(DqState<D>& st, const char* Ks, const c
       dsb[2 * n2 + (i >> 3)][i & 7] = (bf16)(pr * (dp[n2][i] - st.Drow));
     }
   }
+  // (addresses from lds_byte here: the shared TileReadOffsets bases made this
+  // kernel's schedule slower)
   const int gi = l & 15;
   const int dsub = 16 * ((l >> 4) & 1);
 #pragma unroll
@@ -256,21 +258,19 @@ struct DkvState {
 template <int D>
 __device__ __forceinline__ void dkdv_block(DkvState<D>& st, const char* Qs, const char* dOs, const float* l2s,
                                            const float* Ds, int32_t qs, int32_t L, int32_t key, int32_t wk_lo,
-                                           float c2, int h, int lq, int l) {
+                                           float c2, int h, const TileReadOffsets& o) {
   const char* Qb = reinterpret_cast<const char*>(Qs);
   const char* Ob = reinterpret_cast<const char*>(dOs);
-  const int gi = l & 15;
-  const int dsub = 16 * ((l >> 4) & 1);
 #pragma unroll
   for (int mq = 0; mq < 2; ++mq) {
     const int32_t qm = qs + 32 * mq;
     if (qm + 31 < wk_lo) continue;  // every query of this half precedes every key of the wave
     f32x16 s = {}, dp = {};
-    const int r = 32 * mq + lq;
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) {
-      const bf16x8 aq = *reinterpret_cast<const bf16x8*>(Qb + lds_byte(r, 16 * kk + 8 * h));
-      const bf16x8 ad = *reinterpret_cast<const bf16x8*>(Ob + lds_byte(r, 16 * kk + 8 * h));
+      const uint32_t off = row_off(o, kk) + mq * 32 * 128;
+      const bf16x8 aq = *reinterpret_cast<const bf16x8*>(Qb + off);
+      const bf16x8 ad = *reinterpret_cast<const bf16x8*>(Ob + off);
       s = mfma32(aq, st.kf[kk], s);
       dp = mfma32(ad, st.vf[kk], dp);
     }
@@ -297,14 +297,10 @@ __device__ __forceinline__ void dkdv_block(DkvState<D>& st, const char* Qs, cons
     }
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt) {
-      const int col = 32 * dt + dsub + 4 * (gi & 3);
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        const int r0 = 32 * mq + 16 * ks + 4 * h + (gi >> 2);
-        const bf16x8 bo = tr_read8(reinterpret_cast<const bf16*>(Ob + lds_byte(r0, col)),
-                                   reinterpret_cast<const bf16*>(Ob + lds_byte(r0 + 8, col)));
-        const bf16x8 bq = tr_read8(reinterpret_cast<const bf16*>(Qb + lds_byte(r0, col)),
-                                   reinterpret_cast<const bf16*>(Qb + lds_byte(r0 + 8, col)));
+        const bf16x8 bo = col_operand(Ob + mq * 32 * 128, o, ks, dt);
+        const bf16x8 bq = col_operand(Qb + mq * 32 * 128, o, ks, dt);
         st.dva[dt] = mfma32(pa[ks], bo, st.dva[dt]);
         st.dka[dt] = mfma32(da[ks], bq, st.dka[dt]);
       }
@@ -336,24 +332,14 @@ __device__ __forceinline__ void pin(bf16x8& x) {
 
 template <int D>
 __device__ __forceinline__ void dkdv_block_full(DkvState<D>& st, const char* Qs, const char* dOs, const float* l2s,
-                                                const float* Ds, float c2, int h, int lq, int l) {
+                                                const float* Ds, float c2, int h, const TileReadOffsets& o) {
   constexpr int KS = D / 16;
   constexpr int NC = D / 16;
   constexpr int PF = 3;  // operands of the next region read ahead
-  const int gi = l & 15;
-  const int dsub = 16 * ((l >> 4) & 1);
   // A operand of S/dP: row 32*mq + lq, k-step kk
-  auto offA = [&](int mq, int kk) { return lds_byte(32 * mq + lq, 16 * kk + 8 * h); };
-  // B operand of dV/dK, pair c = ks * (D/32) + dt: rows r0, r0 + 8 of column col
-  auto offC0 = [&](int mq, int c) {
-    return lds_byte(32 * mq + 16 * (c / (D / 32)) + 4 * h + (gi >> 2), 32 * (c % (D / 32)) + dsub + 4 * (gi & 3));
-  };
-  auto offC1 = [&](int mq, int c) {
-    return lds_byte(32 * mq + 16 * (c / (D / 32)) + 4 * h + (gi >> 2) + 8, 32 * (c % (D / 32)) + dsub + 4 * (gi & 3));
-  };
-  auto trC = [&](const char* M, int mq, int c) {
-    return tr_read8(reinterpret_cast<const bf16*>(M + offC0(mq, c)), reinterpret_cast<const bf16*>(M + offC1(mq, c)));
-  };
+  auto offA = [&](int mq, int kk) { return row_off(o, kk) + mq * 32 * 128; };
+  // B operand of dV/dK, pair c = ks * (D/32) + dt: column read of rows 32*mq + 16*ks ..
+  auto trC = [&](const char* M, int mq, int c) { return col_operand(M + mq * 32 * 128, o, c / (D / 32), c % (D / 32)); };
   auto pds = [&](const f32x16& s, const f32x16& dp, const f32x4* l4, const f32x4* d4, bf16x8* pa, bf16x8* da) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -551,6 +537,7 @@ __global__ void __launch_bounds__(kThreads, 1) k_bwd_dkdv(BwdParams p) {
     st.dva[dt] = f32x16{};
   }
   const float c2 = p.scale_log2;
+  const TileReadOffsets ro = tile_read_offsets(h, lq, l);
 
   for (int32_t t = 0; t < niter; t += 2) {
     __builtin_amdgcn_s_waitcnt(0);
@@ -559,9 +546,9 @@ __global__ void __launch_bounds__(kThreads, 1) k_bwd_dkdv(BwdParams p) {
     {
       const int32_t qs = kb + (nqb - 1 - t % nqb) * kBMk;
       if (qs >= wk_lo + 31 && qs + kBMk <= L)
-        dkdv_block_full<D>(st, Qs0, dOs0, l2s0, Ds0, c2, h, lq, l);
+        dkdv_block_full<D>(st, Qs0, dOs0, l2s0, Ds0, c2, h, ro);
       else if (qs + kBMk - 1 >= wk_lo)
-        dkdv_block<D>(st, Qs0, dOs0, l2s0, Ds0, qs, L, key, wk_lo, c2, h, lq, l);
+        dkdv_block<D>(st, Qs0, dOs0, l2s0, Ds0, qs, L, key, wk_lo, c2, h, ro);
     }
     if (t + 1 >= niter) break;
     __builtin_amdgcn_s_waitcnt(0);
@@ -570,9 +557,9 @@ __global__ void __launch_bounds__(kThreads, 1) k_bwd_dkdv(BwdParams p) {
     {
       const int32_t qs = kb + (nqb - 1 - (t + 1) % nqb) * kBMk;
       if (qs >= wk_lo + 31 && qs + kBMk <= L)
-        dkdv_block_full<D>(st, Qs1, dOs1, l2s1, Ds1, c2, h, lq, l);
+        dkdv_block_full<D>(st, Qs1, dOs1, l2s1, Ds1, c2, h, ro);
       else if (qs + kBMk - 1 >= wk_lo)
-        dkdv_block<D>(st, Qs1, dOs1, l2s1, Ds1, qs, L, key, wk_lo, c2, h, lq, l);
+        dkdv_block<D>(st, Qs1, dOs1, l2s1, Ds1, qs, L, key, wk_lo, c2, h, ro);
     }
   }
 

@@ -214,6 +214,51 @@ __device__ __forceinline__ void load_vec64_async(const float* vec, int32_t row0,
 #define PSC_SCHED_MFMA(n) __builtin_amdgcn_sched_group_barrier(0x0008, (n), 0)
 #define PSC_SCHED_VALU(n) __builtin_amdgcn_sched_group_barrier(0x0002, (n), 0)
 
+// Per-lane LDS byte offsets of the two operand read patterns in a tile.  The
+// swizzle depends on row bits 1..3 only, so moving 16 rows down or one column
+// group right is a constant, and a few per-lane bases cover every read; the
+// constants go into the instructions' offset fields instead of registers.
+//   row[k]:    row lq, columns 16k + 8h (k = 0..3) -- the 16-byte MFMA
+//              operand of k-step k; +kGroupBytes per 4 k-steps, +32*128 for
+//              rows 32 + lq
+//   col[e][u]: column read (ds_read_b64_tr_b16) of rows 4h + gi/4 + 8u and
+//              columns 32e + dsub + 4 (gi % 4), gi = lane % 16, dsub =
+//              16 ((lane / 16) % 2); +2048 per 16 rows, +kGroupBytes per 64
+//              columns
+struct TileReadOffsets {
+  uint32_t row[4];
+  uint32_t col[2][2];
+};
+
+__device__ __forceinline__ TileReadOffsets tile_read_offsets(int h, int lq, int l) {
+  TileReadOffsets o;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) o.row[k] = (uint32_t)lds_byte(lq, 16 * k + 8 * h);
+  const int gi = l & 15;
+  const int dsub = 16 * ((l >> 4) & 1);
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+      o.col[e][u] = (uint32_t)lds_byte(4 * h + (gi >> 2) + 8 * u, 32 * e + dsub + 4 * (gi & 3));
+  }
+  return o;
+}
+// Offset of the row operand of k-step kk (lds_byte(lq, 16 kk + 8 h)).
+__device__ __forceinline__ uint32_t row_off(const TileReadOffsets& o, int kk) {
+  return o.row[kk & 3] + (kk >> 2) * kGroupBytes;
+}
+// Offset of column read u of 16-row slice ks and 32-column slice dt
+// (lds_byte(16 ks + 4 h + gi/4 + 8 u, 32 dt + dsub + 4 (gi % 4))).
+__device__ __forceinline__ uint32_t col_off(const TileReadOffsets& o, int u, int ks, int dt) {
+  return o.col[dt & 1][u] + ks * 2048 + (dt >> 1) * kGroupBytes;
+}
+// Column-read operand (two transposing reads) of slice (ks, dt) at tile M.
+__device__ __forceinline__ bf16x8 col_operand(const char* M, const TileReadOffsets& o, int ks, int dt) {
+  return tr_read8(reinterpret_cast<const bf16*>(M + col_off(o, 0, ks, dt)),
+                  reinterpret_cast<const bf16*>(M + col_off(o, 1, ks, dt)));
+}
+
 // acc[n] += A_n B over k = 0..KS-1 for two row blocks n = 0, 1 whose A
 // fragments are 16-byte LDS reads at a0 + off(kk) and a1 + off(kk), with one
 // k-step of read-ahead so every MFMA finds its operands already loaded.

@@ -66,12 +66,12 @@ struct FwdState {
 // One 64-key block for one wave.
 template <int D>
 __device__ __forceinline__ void fwd_block(FwdState<D>& st, const char* Ks, const char* Vs, int32_t kb, int32_t L,
-                                          int32_t qrow, int32_t wq_lo, float c2, int h, int lq, int l) {
+                                          int32_t qrow, int32_t wq_lo, float c2, int h, const TileReadOffsets& o) {
   const char* Kb = reinterpret_cast<const char*>(Ks);
   const char* Vb = reinterpret_cast<const char*>(Vs);
   f32x16 s[2] = {f32x16{}, f32x16{}};
   // rows lq and 32 + lq share the swizzle (it depends on row bits 1..3 only)
-  mfma_rows2<D / 16>(s[0], s[1], Kb, Kb + 32 * 128, st.qf, [&](int kk) { return lds_byte(lq, 16 * kk + 8 * h); });
+  mfma_rows2<D / 16>(s[0], s[1], Kb, Kb + 32 * 128, st.qf, [&](int kk) { return row_off(o, kk); });
   if ((kb + kBN - 1 > wq_lo) || (kb + kBN > L)) {
 #pragma unroll
     for (int n2 = 0; n2 < 2; ++n2) {
@@ -110,18 +110,10 @@ __device__ __forceinline__ void fwd_block(FwdState<D>& st, const char* Ks, const
     }
   }
   st.l_i += rs;
-  const int gi = l & 15;
-  const int dsub = 16 * ((l >> 4) & 1);
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) {
-    const int col = 32 * dt + dsub + 4 * (gi & 3);
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const int r0 = 16 * ks + 4 * h + (gi >> 2);
-      const bf16* p0 = reinterpret_cast<const bf16*>(Vb + lds_byte(r0, col));
-      const bf16* p1 = reinterpret_cast<const bf16*>(Vb + lds_byte(r0 + 8, col));
-      st.oacc[dt] = mfma32(tr_read8(p0, p1), pb[ks], st.oacc[dt]);
-    }
+    for (int ks = 0; ks < 4; ++ks) st.oacc[dt] = mfma32(col_operand(Vb, o, ks, dt), pb[ks], st.oacc[dt]);
   }
 }
 
@@ -173,18 +165,19 @@ __global__ void __launch_bounds__(kThreads, 2) k_attn_fwd(FwdParams p) {
 
   const int32_t wq_lo = q0 + 32 * w, wq_hi = wq_lo + 31;
   const float c2 = p.scale_log2;
+  const TileReadOffsets ro = tile_read_offsets(h, lq, l);
   for (int32_t j = 0; j < nkv; j += 2) {
     // stage 0 holds block j
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (j + 1 < nkv) load_kv<D>(Kp, Vp, p.sk, p.sv, (j + 1) * kBN, L, Ks1, Vs1, koff, voff, w, l);
-    if (j * kBN <= wq_hi) fwd_block<D>(st, Ks0, Vs0, j * kBN, L, qrow, wq_lo, c2, h, lq, l);
+    if (j * kBN <= wq_hi) fwd_block<D>(st, Ks0, Vs0, j * kBN, L, qrow, wq_lo, c2, h, ro);
     if (j + 1 >= nkv) break;
     // stage 1 holds block j + 1
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (j + 2 < nkv) load_kv<D>(Kp, Vp, p.sk, p.sv, (j + 2) * kBN, L, Ks0, Vs0, koff, voff, w, l);
-    if ((j + 1) * kBN <= wq_hi) fwd_block<D>(st, Ks1, Vs1, (j + 1) * kBN, L, qrow, wq_lo, c2, h, lq, l);
+    if ((j + 1) * kBN <= wq_hi) fwd_block<D>(st, Ks1, Vs1, (j + 1) * kBN, L, qrow, wq_lo, c2, h, ro);
   }
 
   // Epilogue.  O goes out through LDS so that each store instruction writes
