@@ -45,9 +45,9 @@ KERNEL_SOURCES = {
 }
 MEASURED_TRAFFIC = {
     # (kernel, workload): (sources sha256 prefix, read bytes, write bytes)
-    ("attn_fwd", "lognormal_32k"): ("b3bacdc59a71e233", 2.0 * 1374493.0 * 1024, 533045.7 * 1024),
-    ("attn_bwd_dkdv", "lognormal_32k"): ("c6650b8699c7464e", 2.0 * 4170252.7 * 1024, 524288.0 * 1024),
-    ("attn_bwd_dq", "lognormal_32k"): ("c6650b8699c7464e", 2.0 * 1891521.2 * 1024, 1070681.0 * 1024),
+    ("attn_fwd", "lognormal_32k"): ("c9c6b9b4d1874965", 2.0 * 1377686.0 * 1024, 1.0 * 533007.6 * 1024),
+    ("attn_bwd_dkdv", "lognormal_32k"): ("4ac467ff9cad89ba", 2.0 * 4167809.8 * 1024, 1.0 * 524288.0 * 1024),
+    ("attn_bwd_dq", "lognormal_32k"): ("4ac467ff9cad89ba", 2.0 * 1918817.8 * 1024, 1.0 * 1066039.5 * 1024),
 }
 
 
