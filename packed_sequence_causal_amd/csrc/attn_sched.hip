@@ -142,11 +142,17 @@ __global__ void __launch_bounds__(kThreads) k_sched_fill(const int32_t* cu, int3
 }
 
 // The whole schedule in one workgroup, for the common sizes (segments, bins
-// and tiles few enough for LDS and one block's loops): the same four stages
-// with the per-segment offsets and the bins in LDS, so one launch replaces
-// four.
+// and tiles few enough for LDS and one block's loops); one launch replaces
+// four.  Prefix mode (forward, dQ) uses a document-major order: documents by
+// decreasing length (counting sort over length bins), each taking a
+// contiguous run of slots with its tiles by decreasing work (last tile
+// first).  The query tiles of one document then run at the same time and
+// read the same key/value prefix blocks together, which L2 serves once;
+// this made the forward and dQ 10-13 % faster on 1-2K-token documents.  Suffix
+// mode (dK/dV) keeps the plain longest-tile-first order, which measured
+// faster there (workgroups of equal length run side by side, one per CU).
 constexpr int kSmallThreads = 1024;
-constexpr int kSmallSeg = 4096;     // n_seg + 1 limit (toff in LDS)
+constexpr int kSmallSeg = 4096;     // n_seg + 1 limit (per-segment tables in LDS)
 constexpr int kSmallBins = 4096;    // n_bins limit (histogram in LDS)
 constexpr int64_t kSmallCap = 131072;
 
@@ -172,11 +178,16 @@ __device__ inline int32_t block_exscan(int32_t v, int32_t* wsum, int32_t& tot) {
   return off + x - v;
 }
 
+__device__ inline int32_t doc_bin(const int32_t* cu, int32_t s, int32_t T, int32_t unit, int32_t n_bins) {
+  return min((seg_len(cu, s, T) + unit - 1) / unit, n_bins - 1);
+}
+
 __global__ void __launch_bounds__(kSmallThreads) k_sched_small(const int32_t* cu, int32_t n_seg, int32_t T,
                                                                int32_t tile, int32_t unit, bool suffix,
                                                                int32_t n_bins, int32_t* items, int64_t cap,
                                                                int32_t* n_items) {
   __shared__ int32_t toff[kSmallSeg];
+  __shared__ int32_t dpos[kSmallSeg];  // prefix mode: first slot of each document's run
   __shared__ int32_t hist[kSmallBins];
   __shared__ int32_t wsum[kSmallThreads / 64];
   for (int32_t i = threadIdx.x; i < n_bins; i += kSmallThreads) hist[i] = 0;
@@ -193,14 +204,20 @@ __global__ void __launch_bounds__(kSmallThreads) k_sched_small(const int32_t* cu
   if (threadIdx.x == 0) toff[n_seg] = carry;
   __syncthreads();
   const int32_t n = (int32_t)min((int64_t)carry, cap);
-  // histogram of work bins
-  for (int32_t i = threadIdx.x; i < n; i += kSmallThreads) {
-    int32_t sg, t;
-    tile_of(toff, n_seg, i, sg, t);
-    atomicAdd(&hist[tile_bin(cu, sg, t, T, tile, unit, suffix, n_bins)], 1);
+  if (suffix) {
+    // longest tile first: histogram of tile work
+    for (int32_t i = threadIdx.x; i < n; i += kSmallThreads) {
+      int32_t sg, t;
+      tile_of(toff, n_seg, i, sg, t);
+      atomicAdd(&hist[tile_bin(cu, sg, t, T, tile, unit, true, n_bins)], 1);
+    }
+  } else {
+    // document-major: tiles per document-length bin
+    for (int32_t sg = threadIdx.x; sg < n_seg; sg += kSmallThreads)
+      atomicAdd(&hist[doc_bin(cu, sg, T, unit, n_bins)], toff[sg + 1] - toff[sg]);
   }
   __syncthreads();
-  // descending exclusive scan: cursor[b] = tiles in bins above b
+  // descending exclusive scan: cursor[b] = tiles of the documents in bins above b
   carry = 0;
   for (int32_t c = 0; c < n_bins; c += kSmallThreads) {
     const int32_t i = c + threadIdx.x;
@@ -212,13 +229,23 @@ __global__ void __launch_bounds__(kSmallThreads) k_sched_small(const int32_t* cu
     carry += tot;
   }
   __syncthreads();
-  // scatter: each tile takes the next slot of its bin
+  if (!suffix) {
+    // each document claims a contiguous run inside its bin
+    for (int32_t sg = threadIdx.x; sg < n_seg; sg += kSmallThreads)
+      dpos[sg] = atomicAdd(&hist[doc_bin(cu, sg, T, unit, n_bins)], toff[sg + 1] - toff[sg]);
+    __syncthreads();
+  }
+  // scatter: suffix mode takes the next slot of the tile's work bin; prefix
+  // mode puts tile t of document sg at its run's slot nt - 1 - t
   for (int32_t i = threadIdx.x; i < n; i += kSmallThreads) {
     int32_t sg, t;
     tile_of(toff, n_seg, i, sg, t);
-    const int32_t pos = atomicAdd(&hist[tile_bin(cu, sg, t, T, tile, unit, suffix, n_bins)], 1);
-    const int32_t a = min(max(cu[sg], 0), T);
-    *reinterpret_cast<int4*>(items + 4 * pos) = make_int4(a, seg_len(cu, sg, T), t, sg);
+    const int32_t pos = suffix ? atomicAdd(&hist[tile_bin(cu, sg, t, T, tile, unit, true, n_bins)], 1)
+                               : dpos[sg] + (toff[sg + 1] - toff[sg]) - 1 - t;
+    if (pos < n) {
+      const int32_t a = min(max(cu[sg], 0), T);
+      *reinterpret_cast<int4*>(items + 4 * pos) = make_int4(a, seg_len(cu, sg, T), t, sg);
+    }
   }
   if (threadIdx.x == 0) *n_items = n;
 }
