@@ -8,6 +8,12 @@ There is no fallback: without the built library every call raises.
 Entry points (same names as the C ABI without the ``psc_`` prefix):
   pack_sizes, pack_build                  build_pack / build_unpack on the GPU
   varlen_attn_workspace, varlen_attn_fwd, varlen_attn_bwd
+                                          document-causal attention (bf16 or fp32)
+  rope                                    rotary embedding at the packer's indexes
+  row_max_seqlen, unpack_data, split_sequence
+                                          data steps after the packer
+  timing_enable, timing_reset, timing_read
+                                          per-kernel HIP-event timing
 """
 from __future__ import annotations
 
