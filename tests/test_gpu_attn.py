@@ -112,6 +112,26 @@ def test_bf16_random_layouts(seed):
     full_compare(q, k, v, do, cu, "bf16")
 
 
+# Randomised layouts mixing lengths across the tile edges: long and short
+# documents in one row, so the document-major schedule, tiles whose last key
+# block lands in either LDS stage (odd and even block counts), ragged tails
+# and several GQA ratios are all exercised against the oracle.
+@pytest.mark.parametrize("seed", range(6))
+def test_bf16_mixed_layout_sweep(seed):
+    rng = np.random.default_rng(9000 + seed)
+    lens = list(rng.integers(1, 40, int(rng.integers(3, 12))))
+    lens += list(rng.integers(100, 700, int(rng.integers(2, 5))))
+    lens.append(int(rng.integers(900, 1800)))
+    rng.shuffle(lens)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    T = int(cu[-1])
+    D = [64, 128][seed % 2]
+    hkv = [1, 2, 4][seed % 3]
+    hq = hkv * [1, 2, 4][(seed // 2) % 3]
+    q, k, v, do = workloads.qkv_do(T, hq, hkv, D, seed=seed, dtype="bf16")
+    full_compare(q, k, v, do, cu, "bf16")
+
+
 @pytest.mark.parametrize("factor", [0.5, 1.25])
 def test_bf16_explicit_softmax_scale(factor):
     # the scale argument is honoured (a factor around the default 1/sqrt(D));
