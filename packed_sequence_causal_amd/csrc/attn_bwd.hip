@@ -252,65 +252,13 @@ struct DkvState {
   f32x16 dka[D / 32], dva[D / 32];
 };
 
-// One 64-query block of the dK/dV loop for one wave (keys wk_lo .. wk_lo+31,
-// this lane's key `key`) that needs the mask: the blocks on the diagonal and
-// the last block of a document.  Unmasked blocks take dkdv_block_full.
-template <int D>
-__device__ __forceinline__ void dkdv_block(DkvState<D>& st, const char* Qs, const char* dOs, const float* l2s,
-                                           const float* Ds, int32_t qs, int32_t L, int32_t key, int32_t wk_lo,
-                                           float c2, int h, const TileReadOffsets& o) {
-  const char* Qb = reinterpret_cast<const char*>(Qs);
-  const char* Ob = reinterpret_cast<const char*>(dOs);
-#pragma unroll
-  for (int mq = 0; mq < 2; ++mq) {
-    const int32_t qm = qs + 32 * mq;
-    if (qm + 31 < wk_lo) continue;  // every query of this half precedes every key of the wave
-    f32x16 s = {}, dp = {};
-#pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) {
-      const uint32_t off = row_off(o, kk) + mq * 32 * 128;
-      const bf16x8 aq = *reinterpret_cast<const bf16x8*>(Qb + off);
-      const bf16x8 ad = *reinterpret_cast<const bf16x8*>(Ob + off);
-      s = mfma32(aq, st.kf[kk], s);
-      dp = mfma32(ad, st.vf[kk], dp);
-    }
-    // s[i], dp[i] <-> query 32*mq + 8*(i/4) + 4*h + i%4 of the block, key = this lane's key
-    if ((qm < wk_lo + 31) || (qm + 32 > L)) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int32_t qa = qm + 8 * (i >> 2) + 4 * h + (i & 3);
-        if (qa < key || qa >= L) s[i] = -INFINITY;
-      }
-    }
-    bf16x8 pa[2], da[2];
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const f32x4 l4 = *reinterpret_cast<const f32x4*>(l2s + 32 * mq + 8 * g + 4 * h);
-      const f32x4 d4 = *reinterpret_cast<const f32x4*>(Ds + 32 * mq + 8 * g + 4 * h);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int i = 4 * g + e;
-        const float pr = fast_exp2(__builtin_fmaf(s[i], c2, -l4[e]));
-        pa[i >> 3][i & 7] = (bf16)pr;
-        da[i >> 3][i & 7] = (bf16)(pr * (dp[i] - d4[e]));
-      }
-    }
-#pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt) {
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const bf16x8 bo = col_operand(Ob + mq * 32 * 128, o, ks, dt);
-        const bf16x8 bq = col_operand(Qb + mq * 32 * 128, o, ks, dt);
-        st.dva[dt] = mfma32(pa[ks], bo, st.dva[dt]);
-        st.dka[dt] = mfma32(da[ks], bq, st.dka[dt]);
-      }
-    }
-  }
-}
-
-// The unmasked block, software-pipelined inside one wave (at one wave per
-// SIMD nothing else fills the matrix core while a wave waits).  Per 32-query
-// half mq the work is
+// One 64-query block of the dK/dV loop for one wave (keys wk_lo .. +31, this
+// lane's key `key`), software-pipelined inside the wave (at one wave per SIMD
+// nothing else fills the matrix core while a wave waits).  Blocks on the
+// diagonal or at the document end (MASK) take the same schedule with the
+// mask applied to S just before B; a half whose queries all precede the
+// wave's keys is computed and then fully masked (cheaper than a separate,
+// unscheduled path).  Per 32-query half mq the work is
 //   A(mq): S and dP (16 MFMAs, operand rows read from LDS)
 //   B(mq): P and dS in bf16, laid out as the A operand of the next products
 //   C(mq): dV += P^T dO and dK += dS^T Q (16 MFMAs, column reads from LDS)
@@ -330,9 +278,21 @@ __device__ __forceinline__ void pin(bf16x8& x) {
   x = __builtin_bit_cast(bf16x8, t);
 }
 
-template <int D>
+// Scores of query half qm (queries qm + 8 (i / 4) + 4 h + i % 4 of register
+// i) before this lane's key or at/after the document end get -inf.
+__device__ __forceinline__ void mask_half(f32x16& s, int32_t qm, int32_t key, int32_t L, int h) {
+  const int32_t lo = key - qm - 4 * h, hi = L - qm - 4 * h;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int c = 8 * (i >> 2) + (i & 3);
+    if (c < lo || c >= hi) s[i] = -INFINITY;
+  }
+}
+
+template <int D, bool MASK>
 __device__ __forceinline__ void dkdv_block_full(DkvState<D>& st, const char* Qs, const char* dOs, const float* l2s,
-                                                const float* Ds, float c2, int h, const TileReadOffsets& o) {
+                                                const float* Ds, float c2, int h, const TileReadOffsets& o,
+                                                int32_t qs, int32_t key, int32_t L) {
   constexpr int KS = D / 16;
   constexpr int NC = D / 16;
   constexpr int PF = 3;  // operands of the next region read ahead
@@ -400,6 +360,7 @@ __device__ __forceinline__ void dkdv_block_full(DkvState<D>& st, const char* Qs,
       s1 = mfma32(nq[kk], st.kf[kk], s1);
       dp1 = mfma32(nd[kk], st.vf[kk], dp1);
     }
+    if (MASK) mask_half(s0, qs, key, L, h);
     pds(s0, dp0, l4a, d4a, pa0, da0);
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
@@ -437,6 +398,7 @@ __device__ __forceinline__ void dkdv_block_full(DkvState<D>& st, const char* Qs,
       st.dva[dt] = mfma32(pa0[ks], bo[c], st.dva[dt]);
       st.dka[dt] = mfma32(da0[ks], bq[c], st.dka[dt]);
     }
+    if (MASK) mask_half(s1, qs + 32, key, L, h);
     pds(s1, dp1, l4b, d4b, pa1, da1);
 #pragma unroll
     for (int c = 0; c < PF; ++c) {
@@ -546,9 +508,9 @@ __global__ void __launch_bounds__(kThreads, 1) k_bwd_dkdv(BwdParams p) {
     {
       const int32_t qs = kb + (nqb - 1 - t % nqb) * kBMk;
       if (qs >= wk_lo + 31 && qs + kBMk <= L)
-        dkdv_block_full<D>(st, Qs0, dOs0, l2s0, Ds0, c2, h, ro);
+        dkdv_block_full<D, false>(st, Qs0, dOs0, l2s0, Ds0, c2, h, ro, qs, key, L);
       else if (qs + kBMk - 1 >= wk_lo)
-        dkdv_block<D>(st, Qs0, dOs0, l2s0, Ds0, qs, L, key, wk_lo, c2, h, ro);
+        dkdv_block_full<D, true>(st, Qs0, dOs0, l2s0, Ds0, c2, h, ro, qs, key, L);
     }
     if (t + 1 >= niter) break;
     __builtin_amdgcn_s_waitcnt(0);
@@ -557,9 +519,9 @@ __global__ void __launch_bounds__(kThreads, 1) k_bwd_dkdv(BwdParams p) {
     {
       const int32_t qs = kb + (nqb - 1 - (t + 1) % nqb) * kBMk;
       if (qs >= wk_lo + 31 && qs + kBMk <= L)
-        dkdv_block_full<D>(st, Qs1, dOs1, l2s1, Ds1, c2, h, ro);
+        dkdv_block_full<D, false>(st, Qs1, dOs1, l2s1, Ds1, c2, h, ro, qs, key, L);
       else if (qs + kBMk - 1 >= wk_lo)
-        dkdv_block<D>(st, Qs1, dOs1, l2s1, Ds1, qs, L, key, wk_lo, c2, h, ro);
+        dkdv_block_full<D, true>(st, Qs1, dOs1, l2s1, Ds1, c2, h, ro, qs, key, L);
     }
   }
 
