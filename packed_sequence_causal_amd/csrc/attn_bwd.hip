@@ -81,12 +81,14 @@ __device__ __forceinline__ void dq_block(DqState<D>& st, const char* Ks, const c
     }
   }
   if ((kb + kBNq - 1 > wq_lo) || (kb + kBNq > L)) {
+    // key kb + 32 n2 + 8 (i / 4) + 4 h + i % 4 is masked when it is after the
+    // row or at/after the document end: one compare with a constant per score
+    const int32_t lim = min(qrow + 1, L) - kb - 4 * h;
 #pragma unroll
     for (int n2 = 0; n2 < 2; ++n2) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const int32_t key = kb + 32 * n2 + 8 * (i >> 2) + 4 * h + (i & 3);
-        if (key > qrow || key >= L) s[n2][i] = -INFINITY;
+        if (32 * n2 + 8 * (i >> 2) + (i & 3) >= lim) s[n2][i] = -INFINITY;
       }
     }
   }

@@ -73,12 +73,14 @@ __device__ __forceinline__ void fwd_block(FwdState<D>& st, const char* Ks, const
   // rows lq and 32 + lq share the swizzle (it depends on row bits 1..3 only)
   mfma_rows2<D / 16>(s[0], s[1], Kb, Kb + 32 * 128, st.qf, [&](int kk) { return row_off(o, kk); });
   if ((kb + kBN - 1 > wq_lo) || (kb + kBN > L)) {
+    // key kb + 32 n2 + 8 (i / 4) + 4 h + i % 4 is masked when it is after the
+    // row or at/after the document end: one compare with a constant per score
+    const int32_t lim = min(qrow + 1, L) - kb - 4 * h;
 #pragma unroll
     for (int n2 = 0; n2 < 2; ++n2) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const int32_t key = kb + 32 * n2 + 8 * (i >> 2) + 4 * h + (i & 3);
-        if (key > qrow || key >= L) s[n2][i] = -INFINITY;
+        if (32 * n2 + 8 * (i >> 2) + (i & 3) >= lim) s[n2][i] = -INFINITY;
       }
     }
   }
