@@ -45,9 +45,9 @@ KERNEL_SOURCES = {
 }
 MEASURED_TRAFFIC = {
     # (kernel, workload): (sources sha256 prefix, read bytes, write bytes)
-    ("attn_fwd", "lognormal_32k"): ("c9c6b9b4d1874965", 2.0 * 1377686.0 * 1024, 1.0 * 533007.6 * 1024),
-    ("attn_bwd_dkdv", "lognormal_32k"): ("4ac467ff9cad89ba", 2.0 * 4167809.8 * 1024, 1.0 * 524288.0 * 1024),
-    ("attn_bwd_dq", "lognormal_32k"): ("4ac467ff9cad89ba", 2.0 * 1918817.8 * 1024, 1.0 * 1066039.5 * 1024),
+    ("attn_fwd", "lognormal_32k"): ("b2dea1f8b19b2fd1", 2.0 * 418225.7 * 1024, 1.0 * 532780.0 * 1024),
+    ("attn_bwd_dkdv", "lognormal_32k"): ("556f7c6d26832f9c", 2.0 * 4137564.5 * 1024, 1.0 * 524288.0 * 1024),
+    ("attn_bwd_dq", "lognormal_32k"): ("556f7c6d26832f9c", 2.0 * 964407.4 * 1024, 1.0 * 1065640.0 * 1024),
 }
 
 
