@@ -264,9 +264,11 @@ struct DkvState {
 //   A(mq): S and dP (16 MFMAs, operand rows read from LDS)
 //   B(mq): P and dS in bf16, laid out as the A operand of the next products
 //   C(mq): dV += P^T dO and dK += dS^T Q (16 MFMAs, column reads from LDS)
-// issued as four regions  A(0) | A(1) + B(0) | C(0) + B(1) | C(1),  so that the
-// VALU work of one half runs between the MFMAs of the other.  Each region
-// ends by reading the first operands of the next one.
+// issued as four regions, B split into its two 16-query slices a and b:
+//   A(0) | A(1) + B(0)a | C(0) + B(0)b + B(1)a | C(1) + B(1)b
+// so that the VALU work of one half runs between the MFMAs of the other (the
+// C MFMAs of slice a go first, those of slice b after its B part).  Each
+// region ends by reading the first operands of the next one.
 #define PSC_SCHED_BARRIER() __builtin_amdgcn_sched_barrier(0)
 
 __device__ __forceinline__ bf16x8 ld8(const char* p) { return *reinterpret_cast<const bf16x8*>(p); }
@@ -302,9 +304,10 @@ __device__ __forceinline__ void dkdv_block_full(DkvState<D>& st, const char* Qs,
   auto offA = [&](int mq, int kk) { return row_off(o, kk) + mq * 32 * 128; };
   // B operand of dV/dK, pair c = ks * (D/32) + dt: column read of rows 32*mq + 16*ks ..
   auto trC = [&](const char* M, int mq, int c) { return col_operand(M + mq * 32 * 128, o, c / (D / 32), c % (D / 32)); };
-  auto pds = [&](const f32x16& s, const f32x16& dp, const f32x4* l4, const f32x4* d4, bf16x8* pa, bf16x8* da) {
+  auto pds = [&](const f32x16& s, const f32x16& dp, const f32x4* l4, const f32x4* d4, bf16x8* pa, bf16x8* da,
+                 int i0 = 0, int i1 = 16) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
+    for (int i = i0; i < i1; ++i) {
       const float pr = fast_exp2(__builtin_fmaf(s[i], c2, -l4[i >> 2][i & 3]));
       pa[i >> 3][i & 7] = (bf16)pr;
       da[i >> 3][i & 7] = (bf16)(pr * (dp[i] - d4[i >> 2][i & 3]));
@@ -347,7 +350,7 @@ __device__ __forceinline__ void dkdv_block_full(DkvState<D>& st, const char* Qs,
     PSC_SCHED_DS_READ(8 + 2 * PF);
   }
   PSC_SCHED_BARRIER();
-  // ---------------- region 2: A(1) + B(0)
+  // ---------------- region 2: A(1) + B(0)a
   bf16x8 pa0[2], da0[2];
   bf16x8 cb[PF], cq[PF];        // C(0) operands
   f32x4 l4b[4], d4b[4];         // B(1) row constants
@@ -363,7 +366,7 @@ __device__ __forceinline__ void dkdv_block_full(DkvState<D>& st, const char* Qs,
       dp1 = mfma32(nd[kk], st.vf[kk], dp1);
     }
     if (MASK) mask_half(s0, qs, key, L, h);
-    pds(s0, dp0, l4a, d4a, pa0, da0);
+    pds(s0, dp0, l4a, d4a, pa0, da0, 0, 8);
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       l4b[g] = *reinterpret_cast<const f32x4*>(l2s + 32 + 8 * g + 4 * h);
@@ -382,9 +385,9 @@ __device__ __forceinline__ void dkdv_block_full(DkvState<D>& st, const char* Qs,
     }
     PSC_SCHED_DS_READ(8 + 4 * PF);
   }
-  pin(pa0[0]); pin(pa0[1]); pin(da0[0]); pin(da0[1]);
+  pin(pa0[0]); pin(da0[0]);
   PSC_SCHED_BARRIER();
-  // ---------------- region 3: C(0) + B(1)
+  // ---------------- region 3: C(0) + B(0)b + B(1)a
   bf16x8 pa1[2], da1[2];
   bf16x8 eb[PF], eq[PF];        // C(1) operands
   {
@@ -395,13 +398,20 @@ __device__ __forceinline__ void dkdv_block_full(DkvState<D>& st, const char* Qs,
       bq[c] = c < PF ? cq[c] : trC(Qs, 0, c);
     }
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      const int ks = c / (D / 32), dt = c % (D / 32);
-      st.dva[dt] = mfma32(pa0[ks], bo[c], st.dva[dt]);
-      st.dka[dt] = mfma32(da0[ks], bq[c], st.dka[dt]);
+    for (int c = 0; c < NC / 2; ++c) {
+      const int dt = c % (D / 32);
+      st.dva[dt] = mfma32(pa0[0], bo[c], st.dva[dt]);
+      st.dka[dt] = mfma32(da0[0], bq[c], st.dka[dt]);
+    }
+    pds(s0, dp0, l4a, d4a, pa0, da0, 8, 16);
+#pragma unroll
+    for (int c = NC / 2; c < NC; ++c) {
+      const int dt = c % (D / 32);
+      st.dva[dt] = mfma32(pa0[1], bo[c], st.dva[dt]);
+      st.dka[dt] = mfma32(da0[1], bq[c], st.dka[dt]);
     }
     if (MASK) mask_half(s1, qs + 32, key, L, h);
-    pds(s1, dp1, l4b, d4b, pa1, da1);
+    pds(s1, dp1, l4b, d4b, pa1, da1, 0, 8);
 #pragma unroll
     for (int c = 0; c < PF; ++c) {
       eb[c] = trC(dOs, 1, c);
@@ -414,9 +424,9 @@ __device__ __forceinline__ void dkdv_block_full(DkvState<D>& st, const char* Qs,
       PSC_SCHED_VALU(kDkdvValuPerMfma);
     }
   }
-  pin(pa1[0]); pin(pa1[1]); pin(da1[0]); pin(da1[1]);
+  pin(pa1[0]); pin(da1[0]);
   PSC_SCHED_BARRIER();
-  // ---------------- region 4: C(1)
+  // ---------------- region 4: C(1) + B(1)b
   {
     bf16x8 bo[NC], bq[NC];
 #pragma unroll
@@ -425,16 +435,24 @@ __device__ __forceinline__ void dkdv_block_full(DkvState<D>& st, const char* Qs,
       bq[c] = c < PF ? eq[c] : trC(Qs, 1, c);
     }
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      const int ks = c / (D / 32), dt = c % (D / 32);
-      st.dva[dt] = mfma32(pa1[ks], bo[c], st.dva[dt]);
-      st.dka[dt] = mfma32(da1[ks], bq[c], st.dka[dt]);
+    for (int c = 0; c < NC / 2; ++c) {
+      const int dt = c % (D / 32);
+      st.dva[dt] = mfma32(pa1[0], bo[c], st.dva[dt]);
+      st.dka[dt] = mfma32(da1[0], bq[c], st.dka[dt]);
+    }
+    pds(s1, dp1, l4b, d4b, pa1, da1, 8, 16);
+#pragma unroll
+    for (int c = NC / 2; c < NC; ++c) {
+      const int dt = c % (D / 32);
+      st.dva[dt] = mfma32(pa1[1], bo[c], st.dva[dt]);
+      st.dka[dt] = mfma32(da1[1], bq[c], st.dka[dt]);
     }
     PSC_SCHED_DS_READ(4);
 #pragma unroll
     for (int i = 0; i < 2 * NC; ++i) {
       PSC_SCHED_MFMA(1);
       PSC_SCHED_DS_READ(2);
+      if (i < NC) PSC_SCHED_VALU(2 * kDkdvValuPerMfma);
     }
   }
   PSC_SCHED_BARRIER();
