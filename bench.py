@@ -45,9 +45,9 @@ KERNEL_SOURCES = {
 }
 MEASURED_TRAFFIC = {
     # (kernel, workload): (sources sha256 prefix, read bytes, write bytes)
-    ("attn_fwd", "lognormal_32k"): ("b2dea1f8b19b2fd1", 2.0 * 418225.7 * 1024, 1.0 * 532780.0 * 1024),
-    ("attn_bwd_dkdv", "lognormal_32k"): ("556f7c6d26832f9c", 2.0 * 4137564.5 * 1024, 1.0 * 524288.0 * 1024),
-    ("attn_bwd_dq", "lognormal_32k"): ("556f7c6d26832f9c", 2.0 * 964407.4 * 1024, 1.0 * 1065640.0 * 1024),
+    ("attn_fwd", "lognormal_32k"): ("b2dea1f8b19b2fd1", 2.0 * 419200.4 * 1024, 1.0 * 532791.7 * 1024),
+    ("attn_bwd_dkdv", "lognormal_32k"): ("bc9574ffea12a18c", 2.0 * 4175253.9 * 1024, 1.0 * 524288.0 * 1024),
+    ("attn_bwd_dq", "lognormal_32k"): ("bc9574ffea12a18c", 2.0 * 965399.7 * 1024, 1.0 * 1065648.8 * 1024),
 }
 
 
