@@ -203,7 +203,9 @@ int psc_rope(int dtype, void* q, int64_t q_tok_stride, int32_t hq, void* k, int6
  *   q   [T, hq,  D] ; k, v [T, hkv, D] ; out, dout [T, hq, D]
  * Each is addressed as base + t*tok_stride + h*D + d (strides in elements), so
  * q, k, v may be views into one packed qkv buffer.  tok_stride >= heads*D;
- * for PSC_BF16, base and tok_stride*2 must be multiples of 16 bytes.
+ * for PSC_BF16, base and tok_stride*2 must be multiples of 16 bytes and
+ * tok_stride at most 2^25 elements (a 64-row tile's byte offsets fit 32 bits);
+ * otherwise PSC_ERR_INVALID.
  * cu_seqlens int32 [n_segments + 1]: 0 = c_0 < c_1 < ... < c_n = T (strictly
  * increasing; precondition, not checked on the device).  max_seqlen >= the
  * longest segment (used for scratch sizing only; never for addressing).
@@ -241,6 +243,8 @@ int psc_varlen_attn_fwd(int dtype, const void* q, const void* k, const void* v,
 /*
  * psc_varlen_attn_bwd — gradients of sum(dout * out) for the forward above.
  *   out, lse: the forward's outputs for the same inputs.
+ *   The workspace also carries D_i = <dout_i, out_i> and lse * log2(e)
+ *   between the two kernels of the pass (dQ first, then dK/dV).
  *   dq [T, hq, D], dk [T, hkv, D], dv [T, hkv, D]: float32, contiguous
  *   (token stride heads*D).  dk and dv sum over the hq/hkv query heads of
  *   each key/value head.  All three are written in full.
