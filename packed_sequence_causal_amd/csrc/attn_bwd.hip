@@ -2,7 +2,7 @@
 //
 // Gradients of sum(dO * O) for O = softmax(scale * Q K^T restricted to each
 // document's causal triangle) V, with P recomputed from the forward's lse:
-//   D_i   = <dO_i, O_i>                      (in k_bwd_dq, stored with lse_i *
+//   D_i   = <dO_i, O_i>                      (in k_bwd_dq, stored negated with lse_i *
 //                                              log2 e for k_bwd_dkdv, which
 //                                              runs after it)
 //   P     = exp(scale * q_i.k_j - lse_i)      (recomputed, exp2 domain)
@@ -40,7 +40,7 @@ constexpr int kDkdvValuPerMfma = 4;  // VALU instructions placed after each MFMA
 struct BwdParams {
   const bf16 *q, *k, *v, *o, *dout;
   const float* lse;
-  float* Dbuf;   // [hq][T]  D_i
+  float* Dbuf;   // [hq][T]  -D_i
   float* L2buf;  // [hq][T]  lse_i * log2(e)
   float *dq, *dk, *dv;
   int64_t sq, sk, sv, so, sdo, T;
@@ -181,7 +181,7 @@ __global__ void __launch_bounds__(kThreads, 2) k_bwd_dq(BwdParams p) {
     st.Drow = sum_halves(dacc);
     st.lse2 = qvalid ? p.lse[(int64_t)head * p.T + s0 + qrow] * kLog2e : 0.f;
     if (qvalid && h == 0) {
-      p.Dbuf[(int64_t)head * p.T + s0 + qrow] = st.Drow;
+      p.Dbuf[(int64_t)head * p.T + s0 + qrow] = -st.Drow;
       p.L2buf[(int64_t)head * p.T + s0 + qrow] = st.lse2;
     }
   }
@@ -304,20 +304,35 @@ __device__ __forceinline__ void dkdv_block_full(DkvState<D>& st, const char* Qs,
   auto offA = [&](int mq, int kk) { return row_off(o, kk) + mq * 32 * 128; };
   // B operand of dV/dK, pair c = ks * (D/32) + dt: column read of rows 32*mq + 16*ks ..
   auto trC = [&](const char* M, int mq, int c) { return col_operand(M + mq * 32 * 128, o, c / (D / 32), c % (D / 32)); };
-  auto pds = [&](const f32x16& s, const f32x16& dp, const f32x4* l4, const f32x4* d4, bf16x8* pa, bf16x8* da,
-                 int i0 = 0, int i1 = 16) {
+  // dp already holds dP - D: its accumulator starts from -D (see below)
+  auto pds = [&](const f32x16& s, const f32x16& dp, const f32x4* l4, bf16x8* pa, bf16x8* da, int i0 = 0,
+                 int i1 = 16) {
 #pragma unroll
     for (int i = i0; i < i1; ++i) {
       const float pr = fast_exp2(__builtin_fmaf(s[i], c2, -l4[i >> 2][i & 3]));
       pa[i >> 3][i & 7] = (bf16)pr;
-      da[i >> 3][i & 7] = (bf16)(pr * (dp[i] - d4[i >> 2][i & 3]));
+      da[i >> 3][i & 7] = (bf16)(pr * dp[i]);
     }
+  };
+  // -D of this lane's 16 query rows of half mq (register i <-> query
+  // 8 (i / 4) + 4 h + i % 4), the starting value of the dP accumulator
+  auto negD = [&](int mq) {
+    f32x16 r;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(Ds + 32 * mq + 8 * g + 4 * h);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) r[4 * g + e] = v[e];
+    }
+    return r;
   };
 
   // ---------------- region 1: A(0)
-  f32x16 s0 = {}, dp0 = {}, s1 = {}, dp1 = {};
+  f32x16 s0 = {}, s1 = {};
+  f32x16 dp0 = negD(0);
+  f32x16 dp1;
   bf16x8 nq[KS], nd[KS];        // A(1) operands
-  f32x4 l4a[4], d4a[4];         // B(0) row constants
+  f32x4 l4a[4];                 // B(0) row constants
   {
     bf16x8 aq[KS], ad[KS];
 #pragma unroll
@@ -331,29 +346,27 @@ __device__ __forceinline__ void dkdv_block_full(DkvState<D>& st, const char* Qs,
       dp0 = mfma32(ad[kk], st.vf[kk], dp0);
     }
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      l4a[g] = *reinterpret_cast<const f32x4*>(l2s + 8 * g + 4 * h);
-      d4a[g] = *reinterpret_cast<const f32x4*>(Ds + 8 * g + 4 * h);
-    }
+    for (int g = 0; g < 4; ++g) l4a[g] = *reinterpret_cast<const f32x4*>(l2s + 8 * g + 4 * h);
+    dp1 = negD(1);
 #pragma unroll
     for (int kk = 0; kk < PF; ++kk) {
       nq[kk] = ld8(Qs + offA(1, kk));
       nd[kk] = ld8(dOs + offA(1, kk));
     }
-    // eight operand reads ahead of the first MFMA, then one per MFMA
-    PSC_SCHED_DS_READ(8);
+    // -D and eight operand reads ahead of the first MFMA, then one per MFMA
+    PSC_SCHED_DS_READ(12);
 #pragma unroll
     for (int i = 0; i < 2 * KS; ++i) {
       PSC_SCHED_MFMA(1);
       if (i < 2 * KS - 4) PSC_SCHED_DS_READ(1);
     }
-    PSC_SCHED_DS_READ(8 + 2 * PF);
+    PSC_SCHED_DS_READ(8 + 4 + 2 * PF);
   }
   PSC_SCHED_BARRIER();
   // ---------------- region 2: A(1) + B(0)a
   bf16x8 pa0[2], da0[2];
   bf16x8 cb[PF], cq[PF];        // C(0) operands
-  f32x4 l4b[4], d4b[4];         // B(1) row constants
+  f32x4 l4b[4];                 // B(1) row constants
   {
 #pragma unroll
     for (int kk = PF; kk < KS; ++kk) {
@@ -366,12 +379,9 @@ __device__ __forceinline__ void dkdv_block_full(DkvState<D>& st, const char* Qs,
       dp1 = mfma32(nd[kk], st.vf[kk], dp1);
     }
     if (MASK) mask_half(s0, qs, key, L, h);
-    pds(s0, dp0, l4a, d4a, pa0, da0, 0, 8);
+    pds(s0, dp0, l4a, pa0, da0, 0, 8);
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      l4b[g] = *reinterpret_cast<const f32x4*>(l2s + 32 + 8 * g + 4 * h);
-      d4b[g] = *reinterpret_cast<const f32x4*>(Ds + 32 + 8 * g + 4 * h);
-    }
+    for (int g = 0; g < 4; ++g) l4b[g] = *reinterpret_cast<const f32x4*>(l2s + 32 + 8 * g + 4 * h);
 #pragma unroll
     for (int c = 0; c < PF; ++c) {
       cb[c] = trC(dOs, 0, c);
@@ -403,7 +413,7 @@ __device__ __forceinline__ void dkdv_block_full(DkvState<D>& st, const char* Qs,
       st.dva[dt] = mfma32(pa0[0], bo[c], st.dva[dt]);
       st.dka[dt] = mfma32(da0[0], bq[c], st.dka[dt]);
     }
-    pds(s0, dp0, l4a, d4a, pa0, da0, 8, 16);
+    pds(s0, dp0, l4a, pa0, da0, 8, 16);
 #pragma unroll
     for (int c = NC / 2; c < NC; ++c) {
       const int dt = c % (D / 32);
@@ -411,7 +421,7 @@ __device__ __forceinline__ void dkdv_block_full(DkvState<D>& st, const char* Qs,
       st.dka[dt] = mfma32(da0[1], bq[c], st.dka[dt]);
     }
     if (MASK) mask_half(s1, qs + 32, key, L, h);
-    pds(s1, dp1, l4b, d4b, pa1, da1, 0, 8);
+    pds(s1, dp1, l4b, pa1, da1, 0, 8);
 #pragma unroll
     for (int c = 0; c < PF; ++c) {
       eb[c] = trC(dOs, 1, c);
@@ -440,7 +450,7 @@ __device__ __forceinline__ void dkdv_block_full(DkvState<D>& st, const char* Qs,
       st.dva[dt] = mfma32(pa1[0], bo[c], st.dva[dt]);
       st.dka[dt] = mfma32(da1[0], bq[c], st.dka[dt]);
     }
-    pds(s1, dp1, l4b, d4b, pa1, da1, 8, 16);
+    pds(s1, dp1, l4b, pa1, da1, 8, 16);
 #pragma unroll
     for (int c = NC / 2; c < NC; ++c) {
       const int dt = c % (D / 32);

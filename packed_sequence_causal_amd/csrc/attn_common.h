@@ -86,12 +86,17 @@ __device__ __forceinline__ void lds_dma16(const void* src, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(src) : "memory", "m0");
 }
 // lds_dma16 with a uniform 64-bit base (SGPRs) and a 32-bit per-lane byte
-// offset: the address needs no per-lane arithmetic.
+// offset: the address needs no per-lane arithmetic.  The base often comes
+// from v_readfirstlane just before the statement, and a vector memory
+// instruction may read an SGPR only 5 wait states after a VALU wrote it; the
+// compiler cannot see inside the asm, so the wait states are in it (s_nop 3
+// plus the m0 move).
 __device__ __forceinline__ void lds_dma16_sv(const void* sbase, uint32_t voff, uint32_t lds) {
   const uint64_t a = (uint64_t)(uintptr_t)sbase;
   const uint64_t b = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32)) << 32) |
                      (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a);
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(voff), "s"(b) : "memory", "m0");
+  asm volatile("s_nop 3\n\ts_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(voff), "s"(b)
+               : "memory", "m0");
 }
 __device__ __forceinline__ void lds_dma4(const void* src, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" ::"s"(lds), "v"(src) : "memory", "m0");
