@@ -81,25 +81,29 @@ __device__ __forceinline__ uint32_t xcd_group_remap(uint32_t b, uint32_t n, uint
 // outstanding LDS reads (lgkmcnt(0)) instead of the ones an MFMA needs.
 // Completion is the caller's job: s_waitcnt vmcnt(0) then a barrier before
 // the destination is read, and no read of a destination while it is written.
-// `lds` must be wave-uniform.
+// `lds` must be wave-uniform.  An LDS-DMA load may read M0 only one wait
+// state after a scalar instruction wrote it, hence the s_nop 0.
 __device__ __forceinline__ void lds_dma16(const void* src, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(src) : "memory", "m0");
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(src)
+               : "memory", "m0");
 }
 // lds_dma16 with a uniform 64-bit base (SGPRs) and a 32-bit per-lane byte
 // offset: the address needs no per-lane arithmetic.  The base often comes
 // from v_readfirstlane just before the statement, and a vector memory
 // instruction may read an SGPR only 5 wait states after a VALU wrote it; the
-// compiler cannot see inside the asm, so the wait states are in it (s_nop 3
-// plus the m0 move).
+// compiler cannot see inside the asm, so the wait states are in it (s_nop 2,
+// the m0 move and the s_nop 0 that M0 needs).
 __device__ __forceinline__ void lds_dma16_sv(const void* sbase, uint32_t voff, uint32_t lds) {
   const uint64_t a = (uint64_t)(uintptr_t)sbase;
   const uint64_t b = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32)) << 32) |
                      (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a);
-  asm volatile("s_nop 3\n\ts_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(voff), "s"(b)
+  asm volatile("s_nop 2\n\ts_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(voff),
+               "s"(b)
                : "memory", "m0");
 }
 __device__ __forceinline__ void lds_dma4(const void* src, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" ::"s"(lds), "v"(src) : "memory", "m0");
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off" ::"s"(lds), "v"(src)
+               : "memory", "m0");
 }
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)((PSC_LDS const char*)p);
