@@ -45,9 +45,9 @@ KERNEL_SOURCES = {
 }
 MEASURED_TRAFFIC = {
     # (kernel, workload): (sources sha256 prefix, read bytes, write bytes)
-    ("attn_fwd", "lognormal_32k"): ("b2dea1f8b19b2fd1", 2.0 * 419200.4 * 1024, 1.0 * 532791.7 * 1024),
-    ("attn_bwd_dkdv", "lognormal_32k"): ("bc9574ffea12a18c", 2.0 * 4175253.9 * 1024, 1.0 * 524288.0 * 1024),
-    ("attn_bwd_dq", "lognormal_32k"): ("bc9574ffea12a18c", 2.0 * 965399.7 * 1024, 1.0 * 1065648.8 * 1024),
+    ("attn_fwd", "lognormal_32k"): ("90db9ee62402dd2c", 2.0 * 418766.5 * 1024, 1.0 * 532785.0 * 1024),
+    ("attn_bwd_dkdv", "lognormal_32k"): ("edde6fed378fe087", 2.0 * 4170862.4 * 1024, 1.0 * 524288.0 * 1024),
+    ("attn_bwd_dq", "lognormal_32k"): ("edde6fed378fe087", 2.0 * 965288.6 * 1024, 1.0 * 1065642.4 * 1024),
 }
 
 
