@@ -189,6 +189,8 @@ __global__ void __launch_bounds__(kThreads, 2) k_bwd_dq(BwdParams p) {
   for (int dt = 0; dt < D / 32; ++dt) st.acc[dt] = f32x16{};
 
   const int32_t wq_lo = q0 + 32 * w, wq_hi = wq_lo + 31;
+  // no key blocks for a wave whose rows are all past the document end
+  const int32_t wq_top = wq_lo < L ? wq_hi : -1;
   const float c2 = p.scale_log2;
   for (int32_t j = 0; j < nkv; j += 2) {
     __builtin_amdgcn_s_waitcnt(0);
@@ -197,7 +199,7 @@ __global__ void __launch_bounds__(kThreads, 2) k_bwd_dq(BwdParams p) {
       load_tile<D, kThreads / 64>(Kp, p.sk, (j + 1) * kBNq, L, koff, Ks1, w, l);
       load_tile<D, kThreads / 64>(Vp, p.sv, (j + 1) * kBNq, L, voff, Vs1, w, l);
     }
-    if (j * kBNq <= wq_hi) dq_block<D>(st, Ks0, Vs0, j * kBNq, L, qrow, wq_lo, c2, h, lq, l);
+    if (j * kBNq <= wq_top) dq_block<D>(st, Ks0, Vs0, j * kBNq, L, qrow, wq_lo, c2, h, lq, l);
     if (j + 1 >= nkv) break;
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -205,7 +207,7 @@ __global__ void __launch_bounds__(kThreads, 2) k_bwd_dq(BwdParams p) {
       load_tile<D, kThreads / 64>(Kp, p.sk, (j + 2) * kBNq, L, koff, Ks0, w, l);
       load_tile<D, kThreads / 64>(Vp, p.sv, (j + 2) * kBNq, L, voff, Vs0, w, l);
     }
-    if ((j + 1) * kBNq <= wq_hi) dq_block<D>(st, Ks1, Vs1, (j + 1) * kBNq, L, qrow, wq_lo, c2, h, lq, l);
+    if ((j + 1) * kBNq <= wq_top) dq_block<D>(st, Ks1, Vs1, (j + 1) * kBNq, L, qrow, wq_lo, c2, h, lq, l);
   }
 
   // Epilogue: dQ goes out through LDS so that each store instruction writes
@@ -539,7 +541,7 @@ __global__ void __launch_bounds__(kThreads, 1) k_bwd_dkdv(BwdParams p) {
       const int32_t qs = kb + (nqb - 1 - t % nqb) * kBMk;
       if (qs >= wk_lo + 31 && qs + kBMk <= L)
         dkdv_block_full<D, false>(st, Qs0, dOs0, l2s0, Ds0, c2, h, ro, qs, key, L);
-      else if (qs + kBMk - 1 >= wk_lo)
+      else if (qs + kBMk - 1 >= wk_lo && wk_lo < L)
         dkdv_block_full<D, true>(st, Qs0, dOs0, l2s0, Ds0, c2, h, ro, qs, key, L);
     }
     if (t + 1 >= niter) break;
@@ -550,7 +552,7 @@ __global__ void __launch_bounds__(kThreads, 1) k_bwd_dkdv(BwdParams p) {
       const int32_t qs = kb + (nqb - 1 - (t + 1) % nqb) * kBMk;
       if (qs >= wk_lo + 31 && qs + kBMk <= L)
         dkdv_block_full<D, false>(st, Qs1, dOs1, l2s1, Ds1, c2, h, ro, qs, key, L);
-      else if (qs + kBMk - 1 >= wk_lo)
+      else if (qs + kBMk - 1 >= wk_lo && wk_lo < L)
         dkdv_block_full<D, true>(st, Qs1, dOs1, l2s1, Ds1, c2, h, ro, qs, key, L);
     }
   }

@@ -166,6 +166,9 @@ __global__ void __launch_bounds__(kThreads, 2) k_attn_fwd(FwdParams p) {
   st.l_i = 0.f;
 
   const int32_t wq_lo = q0 + 32 * w, wq_hi = wq_lo + 31;
+  // last key block a wave needs: up to its last row; none when all its rows
+  // are past the document end (the tile's ragged tail)
+  const int32_t wq_top = wq_lo < L ? wq_hi : -1;
   const float c2 = p.scale_log2;
   const TileReadOffsets ro = tile_read_offsets(h, lq, l);
   for (int32_t j = 0; j < nkv; j += 2) {
@@ -173,13 +176,13 @@ __global__ void __launch_bounds__(kThreads, 2) k_attn_fwd(FwdParams p) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (j + 1 < nkv) load_kv<D>(Kp, Vp, p.sk, p.sv, (j + 1) * kBN, L, Ks1, Vs1, koff, voff, w, l);
-    if (j * kBN <= wq_hi) fwd_block<D>(st, Ks0, Vs0, j * kBN, L, qrow, wq_lo, c2, h, ro);
+    if (j * kBN <= wq_top) fwd_block<D>(st, Ks0, Vs0, j * kBN, L, qrow, wq_lo, c2, h, ro);
     if (j + 1 >= nkv) break;
     // stage 1 holds block j + 1
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (j + 2 < nkv) load_kv<D>(Kp, Vp, p.sk, p.sv, (j + 2) * kBN, L, Ks0, Vs0, koff, voff, w, l);
-    if ((j + 1) * kBN <= wq_hi) fwd_block<D>(st, Ks1, Vs1, (j + 1) * kBN, L, qrow, wq_lo, c2, h, ro);
+    if ((j + 1) * kBN <= wq_top) fwd_block<D>(st, Ks1, Vs1, (j + 1) * kBN, L, qrow, wq_lo, c2, h, ro);
   }
 
   // Epilogue.  O goes out through LDS so that each store instruction writes
