@@ -13,9 +13,10 @@
 //                                              query heads and the query blocks
 //                                              from the tile to the document end)
 //   dQ    = scale dS K                        (k_bwd_dq: one workgroup per
-//                                              128-row query tile and query head;
-//                                              loops over key blocks up to the
-//                                              diagonal)
+//                                              query tile and group of HP query
+//                                              heads sharing a key/value head,
+//                                              128 / HP rows; loops over key
+//                                              blocks up to the diagonal)
 // Splitting dQ from dK/dV recomputes S and dP once more but needs no atomics:
 // every output element is written once, and results are deterministic.
 // Both loops visit only tiles inside a document's causal triangle ("Sample
@@ -31,7 +32,7 @@ namespace psc {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kBQ = 128;   // dQ kernel: query rows per workgroup (4 waves x 32)
+constexpr int kBQ = 128;   // dQ kernel: query rows x heads per workgroup (4 waves x 32 rows)
 constexpr int kBNq = 64;   // dQ kernel: keys per block
 constexpr int kBKV = 128;  // dK/dV kernel: keys per workgroup (4 waves x 32)
 constexpr int kBMk = 64;   // dK/dV kernel: queries per block
@@ -119,8 +120,13 @@ __device__ __forceinline__ void dq_block(DqState<D>& st, const char* Ks, const c
   }
 }
 
-template <int D>
+// HP query heads of one key/value group per workgroup (1, 2 or 4), each on
+// 128 / HP rows: wave w takes head w % HP and rows 32 (w / HP) .. +31 of the
+// tile, so with HP = 4 all four waves cover the same rows (equal work) and
+// share every key/value block.
+template <int D, int HP>
 __global__ void __launch_bounds__(kThreads, 2) k_bwd_dq(BwdParams p) {
+  constexpr int RW = kBQ / HP;  // query rows per workgroup
   __shared__ __attribute__((aligned(16))) char Ks0[tile_bytes<D>()];
   __shared__ __attribute__((aligned(16))) char Vs0[tile_bytes<D>()];
   __shared__ __attribute__((aligned(16))) char Ks1[tile_bytes<D>()];
@@ -128,22 +134,25 @@ __global__ void __launch_bounds__(kThreads, 2) k_bwd_dq(BwdParams p) {
 
   const int tid = threadIdx.x, l = tid & 63, h = l >> 5, lq = l & 31;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const uint32_t b = xcd_group_remap(blockIdx.x, gridDim.x, (uint32_t)p.group);
-  const uint32_t item = b / (uint32_t)p.hq, head = b % (uint32_t)p.hq;
-  // item < cap (the grid is cap work-groups per head), so the entry is read
+  const uint32_t ngrp = (uint32_t)(p.hq / HP);  // workgroups per tile
+  const uint32_t b = xcd_group_remap(blockIdx.x, gridDim.x, (uint32_t)(p.group / HP));
+  const uint32_t item = b / ngrp, hg = b % ngrp;
+  const int hw = w % HP, rs = w / HP;
+  const int32_t head = (int32_t)hg * HP + hw;
+  // item < cap (the grid is cap work-groups per head group), so the entry is read
   // together with the count and used only once the count admits it.  Segment
   // bounds come clamped to [0, T] from the schedule: a malformed cu_seqlens
   // cannot send any access outside the tensors.
   const int4 it = *reinterpret_cast<const int4*>(p.items + 4 * item);
   if ((int32_t)item >= *p.n_items) return;
   const int32_t s0 = it.x, L = it.y, tile = it.z;
-  const int32_t q0 = tile * kBQ;
+  const int32_t q0 = tile * RW;
   if (q0 >= L) return;
-  const int32_t kvh = (int32_t)head / p.group;
+  const int32_t kvh = (int32_t)hg * HP / p.group;
 
   const bf16* Kp = p.k + (int64_t)s0 * p.sk + (int64_t)kvh * D;
   const bf16* Vp = p.v + (int64_t)s0 * p.sv + (int64_t)kvh * D;
-  const int32_t kv_end = min(q0 + kBQ, L);
+  const int32_t kv_end = min(q0 + RW, L);
   const int32_t nkv = (kv_end + kBNq - 1) / kBNq;
   uint32_t koff[D / 8 / (kThreads / 64)], voff[D / 8 / (kThreads / 64)];
   tile_offsets<D, kThreads / 64>(p.sk, w, l, koff);
@@ -151,7 +160,7 @@ __global__ void __launch_bounds__(kThreads, 2) k_bwd_dq(BwdParams p) {
   load_tile<D, kThreads / 64>(Kp, p.sk, 0, L, koff, Ks0, w, l);
   load_tile<D, kThreads / 64>(Vp, p.sv, 0, L, voff, Vs0, w, l);
 
-  const int32_t qrow = q0 + 32 * w + lq;
+  const int32_t qrow = q0 + 32 * rs + lq;
   const bool qvalid = qrow < L;
   DqState<D> st;
   {
@@ -188,7 +197,7 @@ __global__ void __launch_bounds__(kThreads, 2) k_bwd_dq(BwdParams p) {
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) st.acc[dt] = f32x16{};
 
-  const int32_t wq_lo = q0 + 32 * w, wq_hi = wq_lo + 31;
+  const int32_t wq_lo = q0 + 32 * rs, wq_hi = wq_lo + 31;
   // no key blocks for a wave whose rows are all past the document end
   const int32_t wq_top = wq_lo < L ? wq_hi : -1;
   const float c2 = p.scale_log2;
@@ -577,9 +586,16 @@ __global__ void __launch_bounds__(kThreads, 1) k_bwd_dkdv(BwdParams p) {
 
 static size_t vec_bytes(const AttnDims& d) { return align_up(sizeof(float) * (size_t)d.hq * d.T, 256); }
 
+// dQ kernel: query heads per workgroup, the largest of 4, 2, 1 that divides
+// the group (its tiles are 128 / that rows high).
+static int dq_heads_per_wg(const AttnDims& d) {
+  const int g = d.hq / d.hkv;
+  return g % 4 == 0 ? 4 : (g % 2 == 0 ? 2 : 1);
+}
+
 size_t attn_bwd_workspace_bytes(int dtype, const AttnDims& d) {
   if (dtype != 1) return vec_bytes(d);
-  return 2 * vec_bytes(d) + schedule_bytes(d.T, d.n_seg, d.max_seqlen, kBQ, kBNq) +
+  return 2 * vec_bytes(d) + schedule_bytes(d.T, d.n_seg, d.max_seqlen, kBQ / dq_heads_per_wg(d), kBNq) +
          schedule_bytes(d.T, d.n_seg, d.max_seqlen, kBKV, kBMk);
 }
 
@@ -590,8 +606,9 @@ hipError_t launch_attn_bwd_bf16(const AttnBwdArgs& a, hipStream_t stream) {
   ws += vec_bytes(d);
   float* L2buf = reinterpret_cast<float*>(ws);
   ws += vec_bytes(d);
-  TileSchedule sq = schedule_carve(ws, d.T, d.n_seg, d.max_seqlen, kBQ, kBNq);
-  ws += schedule_bytes(d.T, d.n_seg, d.max_seqlen, kBQ, kBNq);
+  const int hp = dq_heads_per_wg(d);
+  TileSchedule sq = schedule_carve(ws, d.T, d.n_seg, d.max_seqlen, kBQ / hp, kBNq);
+  ws += schedule_bytes(d.T, d.n_seg, d.max_seqlen, kBQ / hp, kBNq);
   TileSchedule sk = schedule_carve(ws, d.T, d.n_seg, d.max_seqlen, kBKV, kBMk);
 
   BwdParams p;
@@ -621,17 +638,22 @@ hipError_t launch_attn_bwd_bf16(const AttnBwdArgs& a, hipStream_t stream) {
   if (d.T == 0) return hipSuccess;
 
   // dQ first: it also produces D and lse * log2 e, which dK/dV reads.
-  hipError_t e = launch_schedule(a.cu, d.n_seg, (int32_t)d.T, kBQ, kBNq, false, sq, stream);
+  hipError_t e = launch_schedule(a.cu, d.n_seg, (int32_t)d.T, kBQ / hp, kBNq, false, sq, stream);
   if (e != hipSuccess) return e;
   p.items = sq.items;
   p.n_items = sq.n_items;
-  const unsigned grid_q = (unsigned)(sq.cap * d.hq);
+  const unsigned grid_q = (unsigned)(sq.cap * (d.hq / hp));
   {
     ScopedKernelTimer timed(kTimeBwdDq, stream);
-    if (d.d == 128)
-      k_bwd_dq<128><<<grid_q, kThreads, 0, stream>>>(p);
-    else
-      k_bwd_dq<64><<<grid_q, kThreads, 0, stream>>>(p);
+    if (d.d == 128) {
+      if (hp == 4) k_bwd_dq<128, 4><<<grid_q, kThreads, 0, stream>>>(p);
+      else if (hp == 2) k_bwd_dq<128, 2><<<grid_q, kThreads, 0, stream>>>(p);
+      else k_bwd_dq<128, 1><<<grid_q, kThreads, 0, stream>>>(p);
+    } else {
+      if (hp == 4) k_bwd_dq<64, 4><<<grid_q, kThreads, 0, stream>>>(p);
+      else if (hp == 2) k_bwd_dq<64, 2><<<grid_q, kThreads, 0, stream>>>(p);
+      else k_bwd_dq<64, 1><<<grid_q, kThreads, 0, stream>>>(p);
+    }
   }
 
   e = launch_schedule(a.cu, d.n_seg, (int32_t)d.T, kBKV, kBMk, true, sk, stream);

@@ -295,6 +295,19 @@ __device__ __forceinline__ void mfma_rows2(f32x16& acc0, f32x16& acc1, const cha
   PSC_SCHED_MFMA(2);
 }
 
+// acc += A B over k = 0..KS-1 for one row block (mfma_rows2 with a single
+// accumulator), one k-step of read-ahead.
+template <int KS, typename Off>
+__device__ __forceinline__ void mfma_rows1(f32x16& acc, const char* a0, const bf16x8* b, Off off) {
+  bf16x8 x0 = *reinterpret_cast<const bf16x8*>(a0 + off(0));
+#pragma unroll
+  for (int kk = 0; kk < KS; ++kk) {
+    bf16x8 y0 = x0;
+    if (kk + 1 < KS) x0 = *reinterpret_cast<const bf16x8*>(a0 + off(kk + 1));
+    acc = mfma32(y0, b[kk], acc);
+  }
+}
+
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 

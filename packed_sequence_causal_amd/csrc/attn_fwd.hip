@@ -1,7 +1,10 @@
 // Document-causal attention forward, bf16 in / fp32 accumulate, gfx950.
 //
-// One workgroup = one (query tile of 128 rows inside one document, query
-// head).  Four waves own 32 query rows each.  The key/value loop runs over
+// One workgroup = one query tile inside one document for HP query heads of
+// one key/value group (HP = 4, 2 or 1, the largest dividing the group): the
+// tile is 128 / HP rows high and each of the four waves owns 32 rows of one
+// head, so with HP = 4 the waves share rows and key/value blocks and do
+// equal work.  The key/value loop runs over
 // 64-key blocks from the document start to the tile's last row, so only tiles
 // inside the document's causal triangle are visited and no mask is stored
 // ("Sample Packing：长序列 LLM 训练的 Attention 问题及优化", sections 三 and 5.1).
@@ -119,8 +122,13 @@ __device__ __forceinline__ void fwd_block(FwdState<D>& st, const char* Ks, const
   }
 }
 
-template <int D>
+// HP query heads of one key/value group per workgroup (1, 2 or 4), each on
+// 128 / HP rows: wave w takes head w % HP and rows 32 (w / HP) .. +31 of the
+// tile, so with HP = 4 all four waves cover the same rows (equal work) and
+// share every key/value block.
+template <int D, int HP>
 __global__ void __launch_bounds__(kThreads, 2) k_attn_fwd(FwdParams p) {
+  constexpr int RW = kBM / HP;  // query rows per workgroup
   __shared__ __attribute__((aligned(16))) char Ks0[tile_bytes<D>()];
   __shared__ __attribute__((aligned(16))) char Vs0[tile_bytes<D>()];
   __shared__ __attribute__((aligned(16))) char Ks1[tile_bytes<D>()];
@@ -128,8 +136,11 @@ __global__ void __launch_bounds__(kThreads, 2) k_attn_fwd(FwdParams p) {
 
   const int tid = threadIdx.x, l = tid & 63, h = l >> 5, lq = l & 31;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const uint32_t b = xcd_group_remap(blockIdx.x, gridDim.x, (uint32_t)p.group);
-  const uint32_t item = b / (uint32_t)p.hq, head = b % (uint32_t)p.hq;
+  const uint32_t ngrp = (uint32_t)(p.hq / HP);  // workgroups per tile
+  const uint32_t b = xcd_group_remap(blockIdx.x, gridDim.x, (uint32_t)(p.group / HP));
+  const uint32_t item = b / ngrp, hg = b % ngrp;
+  const int hw = w % HP, rs = w / HP;
+  const int32_t head = (int32_t)hg * HP + hw;
   // item < cap (the grid is cap work-groups per head), so the entry is read
   // together with the count and used only once the count admits it.  Segment
   // bounds come clamped to [0, T] from the schedule: a malformed cu_seqlens
@@ -137,22 +148,22 @@ __global__ void __launch_bounds__(kThreads, 2) k_attn_fwd(FwdParams p) {
   const int4 it = *reinterpret_cast<const int4*>(p.items + 4 * item);
   if ((int32_t)item >= *p.n_items) return;
   const int32_t s0 = it.x, L = it.y, tile = it.z;
-  const int32_t q0 = tile * kBM;
+  const int32_t q0 = tile * RW;
   if (q0 >= L) return;
-  const int32_t kvh = (int32_t)head / p.group;
+  const int32_t kvh = (int32_t)hg * HP / p.group;
 
   const bf16* Qp = p.q + (int64_t)s0 * p.sq + (int64_t)head * D;
   const bf16* Kp = p.k + (int64_t)s0 * p.sk + (int64_t)kvh * D;
   const bf16* Vp = p.v + (int64_t)s0 * p.sv + (int64_t)kvh * D;
 
-  const int32_t kv_end = min(q0 + kBM, L);
+  const int32_t kv_end = min(q0 + RW, L);
   const int32_t nkv = (kv_end + kBN - 1) / kBN;
   uint32_t koff[D / 8 / (kThreads / 64)], voff[D / 8 / (kThreads / 64)];
   tile_offsets<D, kThreads / 64>(p.sk, w, l, koff);
   tile_offsets<D, kThreads / 64>(p.sv, w, l, voff);
   load_kv<D>(Kp, Vp, p.sk, p.sv, 0, L, Ks0, Vs0, koff, voff, w, l);
 
-  const int32_t qrow = q0 + 32 * w + lq;
+  const int32_t qrow = q0 + 32 * rs + lq;
   const bool qvalid = qrow < L;
   FwdState<D> st;
 #pragma unroll
@@ -165,7 +176,7 @@ __global__ void __launch_bounds__(kThreads, 2) k_attn_fwd(FwdParams p) {
   st.m_i = -INFINITY;
   st.l_i = 0.f;
 
-  const int32_t wq_lo = q0 + 32 * w, wq_hi = wq_lo + 31;
+  const int32_t wq_lo = q0 + 32 * rs, wq_hi = wq_lo + 31;
   // last key block a wave needs: up to its last row; none when all its rows
   // are past the document end (the tile's ragged tail)
   const int32_t wq_top = wq_lo < L ? wq_hi : -1;
@@ -223,15 +234,22 @@ __global__ void __launch_bounds__(kThreads, 2) k_attn_fwd(FwdParams p) {
 
 }  // namespace
 
+// Query heads per workgroup: the largest of 4, 2, 1 that divides the group.
+static int heads_per_wg(const AttnDims& d) {
+  const int g = d.hq / d.hkv;
+  return g % 4 == 0 ? 4 : (g % 2 == 0 ? 2 : 1);
+}
+
 size_t attn_fwd_workspace_bytes(int dtype, const AttnDims& d) {
   if (dtype != 1) return 256;
-  return schedule_bytes(d.T, d.n_seg, d.max_seqlen, kBM, kBN);
+  return schedule_bytes(d.T, d.n_seg, d.max_seqlen, kBM / heads_per_wg(d), kBN);
 }
 
 hipError_t launch_attn_fwd_bf16(const AttnFwdArgs& a, hipStream_t stream) {
   const AttnDims& d = a.dims;
-  TileSchedule s = schedule_carve(a.workspace, d.T, d.n_seg, d.max_seqlen, kBM, kBN);
-  hipError_t e = launch_schedule(a.cu, d.n_seg, (int32_t)d.T, kBM, kBN, false, s, stream);
+  const int hp = heads_per_wg(d);
+  TileSchedule s = schedule_carve(a.workspace, d.T, d.n_seg, d.max_seqlen, kBM / hp, kBN);
+  hipError_t e = launch_schedule(a.cu, d.n_seg, (int32_t)d.T, kBM / hp, kBN, false, s, stream);
   if (e != hipSuccess) return e;
   FwdParams p;
   p.q = static_cast<const bf16*>(a.q);
@@ -253,10 +271,16 @@ hipError_t launch_attn_fwd_bf16(const AttnFwdArgs& a, hipStream_t stream) {
   const uint64_t grid = (uint64_t)s.cap * (uint64_t)d.hq;
   if (grid == 0) return hipSuccess;
   ScopedKernelTimer timed(kTimeFwd, stream);
-  if (d.d == 128)
-    k_attn_fwd<128><<<(unsigned)grid, kThreads, 0, stream>>>(p);
-  else
-    k_attn_fwd<64><<<(unsigned)grid, kThreads, 0, stream>>>(p);
+  const unsigned g = (unsigned)(grid / hp);
+  if (d.d == 128) {
+    if (hp == 4) k_attn_fwd<128, 4><<<g, kThreads, 0, stream>>>(p);
+    else if (hp == 2) k_attn_fwd<128, 2><<<g, kThreads, 0, stream>>>(p);
+    else k_attn_fwd<128, 1><<<g, kThreads, 0, stream>>>(p);
+  } else {
+    if (hp == 4) k_attn_fwd<64, 4><<<g, kThreads, 0, stream>>>(p);
+    else if (hp == 2) k_attn_fwd<64, 2><<<g, kThreads, 0, stream>>>(p);
+    else k_attn_fwd<64, 1><<<g, kThreads, 0, stream>>>(p);
+  }
   return hipGetLastError();
 }
 
