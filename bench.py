@@ -45,9 +45,9 @@ KERNEL_SOURCES = {
 }
 MEASURED_TRAFFIC = {
     # (kernel, workload): (sources sha256 prefix, read bytes, write bytes)
-    ("attn_fwd", "lognormal_32k"): ("90db9ee62402dd2c", 2.0 * 418766.5 * 1024, 1.0 * 532785.0 * 1024),
-    ("attn_bwd_dkdv", "lognormal_32k"): ("edde6fed378fe087", 2.0 * 4170862.4 * 1024, 1.0 * 524288.0 * 1024),
-    ("attn_bwd_dq", "lognormal_32k"): ("edde6fed378fe087", 2.0 * 965288.6 * 1024, 1.0 * 1065642.4 * 1024),
+    ("attn_fwd", "lognormal_32k"): ("17033b393f969993", 2.0 * 418735.6 * 1024, 1.0 * 533331.6 * 1024),
+    ("attn_bwd_dkdv", "lognormal_32k"): ("cf36e41f146704a6", 2.0 * 4145672.0 * 1024, 1.0 * 524288.0 * 1024),
+    ("attn_bwd_dq", "lognormal_32k"): ("cf36e41f146704a6", 2.0 * 966028.9 * 1024, 1.0 * 1065947.1 * 1024),
 }
 
 
