@@ -37,6 +37,7 @@ constexpr int kBNq = 64;   // dQ kernel: keys per block
 constexpr int kBKV = 128;  // dK/dV kernel: keys per workgroup (4 waves x 32)
 constexpr int kBMk = 64;   // dK/dV kernel: queries per block
 constexpr int kDkdvValuPerMfma = 4;  // VALU instructions placed after each MFMA of the softmax regions
+constexpr int kDqValuPerMfma = 3;    // dQ kernel: VALU instructions after each MFMA of its mixed region
 
 struct BwdParams {
   const bf16 *q, *k, *v, *o, *dout;
@@ -61,57 +62,85 @@ struct DqState {
   float lse2, Drow;
 };
 
-// One 64-key block of the dQ loop for one wave.
+// Keeps the computation of x before this point (IR passes otherwise sink
+// arithmetic past a scheduling barrier, next to its first use).
+__device__ __forceinline__ void pin(bf16x8& x) {
+  typedef int i32x4 __attribute__((ext_vector_type(4)));
+  i32x4 t = __builtin_bit_cast(i32x4, x);
+  asm volatile("" : "+v"(t));
+  x = __builtin_bit_cast(bf16x8, t);
+}
+
+// One 64-key block of the dQ loop for one wave, in two 32-key halves so that
+// the VALU work of one half sits in the same basic block as MFMAs of the
+// other (a diagonal block's mask is a uniform branch, which ends a block):
+//   S, dP of half 0 | [mask 0] | S, dP of half 1 + dS of half 0 (scheduled
+//   together) | [mask 1] |
+//   dS of half 1 + dQ products
 template <int D>
 __device__ __forceinline__ void dq_block(DqState<D>& st, const char* Ks, const char* Vs, int32_t kb, int32_t L,
                                          int32_t qrow, int32_t wq_lo, float c2, int h, int lq, int l) {
   const char* Kb = reinterpret_cast<const char*>(Ks);
   const char* Vb = reinterpret_cast<const char*>(Vs);
-  f32x16 s[2], dp[2];
-#pragma unroll
-  for (int n2 = 0; n2 < 2; ++n2) {
-    s[n2] = f32x16{};
-    dp[n2] = f32x16{};
+  const bool diag = (kb + kBNq - 1 > wq_lo) || (kb + kBNq > L);
+  // key kb + 32 n2 + 8 (i / 4) + 4 h + i % 4 is masked when it is after the
+  // row or at/after the document end: one compare with a constant per score
+  const int32_t lim = min(qrow + 1, L) - kb - 4 * h;
+  const float neg_l = -st.lse2;
+  auto sdp = [&](int n2, f32x16& sa, f32x16& da) {
+    sa = f32x16{};
+    da = f32x16{};
     const int r = 32 * n2 + lq;
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) {
       const bf16x8 ak = *reinterpret_cast<const bf16x8*>(Kb + lds_byte(r, 16 * kk + 8 * h));
       const bf16x8 av = *reinterpret_cast<const bf16x8*>(Vb + lds_byte(r, 16 * kk + 8 * h));
-      s[n2] = mfma32(ak, st.qf[kk], s[n2]);
-      dp[n2] = mfma32(av, st.df[kk], dp[n2]);
+      sa = mfma32(ak, st.qf[kk], sa);
+      da = mfma32(av, st.df[kk], da);
     }
-  }
-  if ((kb + kBNq - 1 > wq_lo) || (kb + kBNq > L)) {
-    // key kb + 32 n2 + 8 (i / 4) + 4 h + i % 4 is masked when it is after the
-    // row or at/after the document end: one compare with a constant per score
-    const int32_t lim = min(qrow + 1, L) - kb - 4 * h;
-#pragma unroll
-    for (int n2 = 0; n2 < 2; ++n2) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        if (32 * n2 + 8 * (i >> 2) + (i & 3) >= lim) s[n2][i] = -INFINITY;
-      }
-    }
-  }
-  const float neg_l = -st.lse2;
-  bf16x8 dsb[4];
-#pragma unroll
-  for (int n2 = 0; n2 < 2; ++n2) {
+  };
+  auto mask = [&](int n2, f32x16& sa) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const float pr = fast_exp2(__builtin_fmaf(s[n2][i], c2, neg_l));
-      dsb[2 * n2 + (i >> 3)][i & 7] = (bf16)(pr * (dp[n2][i] - st.Drow));
+      if (32 * n2 + 8 * (i >> 2) + (i & 3) >= lim) sa[i] = -INFINITY;
     }
+  };
+  auto ds = [&](const f32x16& sa, const f32x16& da, bf16x8* out) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float pr = fast_exp2(__builtin_fmaf(sa[i], c2, neg_l));
+      out[i >> 3][i & 7] = (bf16)(pr * (da[i] - st.Drow));
+    }
+  };
+  f32x16 s0, dp0, s1, dp1;
+  bf16x8 dsb[4];
+  sdp(0, s0, dp0);
+  if (diag) mask(0, s0);
+  // region: S, dP of half 1 (16 MFMAs, 16 row reads) + dS of half 0 (VALU)
+  sdp(1, s1, dp1);
+  ds(s0, dp0, dsb);
+  PSC_SCHED_DS_READ(2);
+#pragma unroll
+  for (int i = 0; i < 2 * (D / 16); ++i) {
+    PSC_SCHED_MFMA(1);
+    if (i < 2 * (D / 16) - 2) PSC_SCHED_DS_READ(1);
+    PSC_SCHED_VALU(kDqValuPerMfma);
   }
+  pin(dsb[0]);
+  pin(dsb[1]);
+  __builtin_amdgcn_sched_barrier(0);
+  if (diag) mask(1, s1);
+  // region: dS of half 1 + dQ products (those of half 0 first)
+  ds(s1, dp1, dsb + 2);
   // (addresses from lds_byte here: the shared TileReadOffsets bases made this
   // kernel's schedule slower)
   const int gi = l & 15;
   const int dsub = 16 * ((l >> 4) & 1);
 #pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt) {
-    const int col = 32 * dt + dsub + 4 * (gi & 3);
+  for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
+    for (int dt = 0; dt < D / 32; ++dt) {
+      const int col = 32 * dt + dsub + 4 * (gi & 3);
       const int r0 = 16 * ks + 4 * h + (gi >> 2);
       const bf16* p0 = reinterpret_cast<const bf16*>(Kb + lds_byte(r0, col));
       const bf16* p1 = reinterpret_cast<const bf16*>(Kb + lds_byte(r0 + 8, col));
@@ -284,14 +313,6 @@ struct DkvState {
 
 __device__ __forceinline__ bf16x8 ld8(const char* p) { return *reinterpret_cast<const bf16x8*>(p); }
 
-// Keeps the computation of x before this point (IR passes otherwise sink
-// arithmetic past a scheduling barrier, next to its first use).
-__device__ __forceinline__ void pin(bf16x8& x) {
-  typedef int i32x4 __attribute__((ext_vector_type(4)));
-  i32x4 t = __builtin_bit_cast(i32x4, x);
-  asm volatile("" : "+v"(t));
-  x = __builtin_bit_cast(bf16x8, t);
-}
 
 // Scores of query half qm (queries qm + 8 (i / 4) + 4 h + i % 4 of register
 // i) before this lane's key or at/after the document end get -inf.
