@@ -500,8 +500,10 @@ __device__ __forceinline__ void dkdv_block_full(DkvState<D>& st, const char* Qs,
   PSC_SCHED_BARRIER();
 }
 
+// D = 128 needs ~370 registers per wave (K, V operands and dK, dV
+// accumulators of 32 keys), one wave per SIMD; D = 64 fits two.
 template <int D>
-__global__ void __launch_bounds__(kThreads, 1) k_bwd_dkdv(BwdParams p) {
+__global__ void __launch_bounds__(kThreads, D == 64 ? 2 : 1) k_bwd_dkdv(BwdParams p) {
   __shared__ __attribute__((aligned(16))) char Qs0[tile_bytes<D>()];
   __shared__ __attribute__((aligned(16))) char dOs0[tile_bytes<D>()];
   __shared__ __attribute__((aligned(16))) char Qs1[tile_bytes<D>()];
