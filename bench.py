@@ -45,9 +45,9 @@ KERNEL_SOURCES = {
 }
 MEASURED_TRAFFIC = {
     # (kernel, workload): (sources sha256 prefix, read bytes, write bytes)
-    ("attn_fwd", "lognormal_32k"): ("17033b393f969993", 2.0 * 418827.9 * 1024, 1.0 * 533346.2 * 1024),
-    ("attn_bwd_dkdv", "lognormal_32k"): ("fb453e062bb24e85", 2.0 * 4161690.1 * 1024, 1.0 * 524288.0 * 1024),
-    ("attn_bwd_dq", "lognormal_32k"): ("fb453e062bb24e85", 2.0 * 965047.8 * 1024, 1.0 * 1065987.1 * 1024),
+    ("attn_fwd", "lognormal_32k"): ("17033b393f969993", 2.0 * 419041.3 * 1024, 1.0 * 533331.7 * 1024),
+    ("attn_bwd_dkdv", "lognormal_32k"): ("4affae70d6718bc4", 2.0 * 4174765.0 * 1024, 1.0 * 524288.0 * 1024),
+    ("attn_bwd_dq", "lognormal_32k"): ("4affae70d6718bc4", 2.0 * 965085.8 * 1024, 1.0 * 1066002.3 * 1024),
 }
 
 
