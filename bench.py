@@ -45,9 +45,9 @@ KERNEL_SOURCES = {
 }
 MEASURED_TRAFFIC = {
     # (kernel, workload): (sources sha256 prefix, read bytes, write bytes)
-    ("attn_fwd", "lognormal_32k"): ("17033b393f969993", 2.0 * 419041.3 * 1024, 1.0 * 533331.7 * 1024),
-    ("attn_bwd_dkdv", "lognormal_32k"): ("4affae70d6718bc4", 2.0 * 4174765.0 * 1024, 1.0 * 524288.0 * 1024),
-    ("attn_bwd_dq", "lognormal_32k"): ("4affae70d6718bc4", 2.0 * 965085.8 * 1024, 1.0 * 1066002.3 * 1024),
+    ("attn_fwd", "lognormal_32k"): ("17033b393f969993", 2.0 * 420238.1 * 1024, 1.0 * 533377.5 * 1024),
+    ("attn_bwd_dkdv", "lognormal_32k"): ("5cb096c7b1a87504", 2.0 * 4193579.1 * 1024, 1.0 * 532863.6 * 1024),
+    ("attn_bwd_dq", "lognormal_32k"): ("5cb096c7b1a87504", 2.0 * 967303.7 * 1024, 1.0 * 1065944.6 * 1024),
 }
 
 

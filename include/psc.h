@@ -243,7 +243,7 @@ int psc_varlen_attn_fwd(int dtype, const void* q, const void* k, const void* v,
 /*
  * psc_varlen_attn_bwd — gradients of sum(dout * out) for the forward above.
  *   out, lse: the forward's outputs for the same inputs.
- *   The workspace also carries -D_i (D_i = <dout_i, out_i>) and lse * log2(e)
+ *   The workspace also carries -D_i (D_i = <dout_i, out_i>) and -lse_i / scale
  *   between the two kernels of the pass (dQ first, then dK/dV).
  *   dq [T, hq, D], dk [T, hkv, D], dv [T, hkv, D]: float32, contiguous
  *   (token stride heads*D).  dk and dv sum over the hq/hkv query heads of

@@ -2,16 +2,19 @@
 //
 // Gradients of sum(dO * O) for O = softmax(scale * Q K^T restricted to each
 // document's causal triangle) V, with P recomputed from the forward's lse:
-//   D_i   = <dO_i, O_i>                      (in k_bwd_dq, stored negated with lse_i *
-//                                              log2 e for k_bwd_dkdv, which
-//                                              runs after it)
+//   D_i   = <dO_i, O_i>                      (in k_bwd_dq, stored negated with
+//                                              -lse_i / scale for k_bwd_dkdv,
+//                                              which runs after it: the two
+//                                              start the dP and S accumulators)
 //   P     = exp(scale * q_i.k_j - lse_i)      (recomputed, exp2 domain)
 //   dP    = dO V^T,   dS = P * (dP - D)
-//   dV    = P^T dO,   dK = scale dS^T Q       (k_bwd_dkdv: one workgroup per
-//                                              128-key tile and key/value head;
-//                                              loops over the head group's
-//                                              query heads and the query blocks
-//                                              from the tile to the document end)
+//   dV    = P^T dO,   dK = scale dS^T Q       (k_bwd_dkdv, D = 64, and
+//                                              k_bwd_dkdv8, D = 128: one
+//                                              workgroup per 128-key tile and
+//                                              key/value head; loops over the
+//                                              head group's query heads and the
+//                                              query blocks from the tile to
+//                                              the document end)
 //   dQ    = scale dS K                        (k_bwd_dq: one workgroup per
 //                                              query tile and group of HP query
 //                                              heads sharing a key/value head,
@@ -43,7 +46,7 @@ struct BwdParams {
   const bf16 *q, *k, *v, *o, *dout;
   const float* lse;
   float* Dbuf;   // [hq][T]  -D_i
-  float* L2buf;  // [hq][T]  lse_i * log2(e)
+  float* NLbuf;  // [hq][T]  -lse_i / scale
   float *dq, *dk, *dv;
   int64_t sq, sk, sv, so, sdo, T;
   const int32_t* cu;
@@ -202,8 +205,8 @@ __global__ void __launch_bounds__(kThreads, 2) k_bwd_dq(BwdParams p) {
     }
   }
   // D_i = <dO_i, O_i> from the dO fragments already held (lanes l and l ^ 32
-  // hold the two halves of row lq) and the same fragments of O; D and
-  // lse * log2 e are also stored for the dK/dV kernel, which runs next.  The
+  // hold the two halves of row lq) and the same fragments of O; -D and
+  // -lse / scale are also stored for the dK/dV kernel, which runs next.  The
   // tiles partition every document, so each (row, head) is written once.
   {
     float dacc = 0.f;
@@ -220,7 +223,7 @@ __global__ void __launch_bounds__(kThreads, 2) k_bwd_dq(BwdParams p) {
     st.lse2 = qvalid ? p.lse[(int64_t)head * p.T + s0 + qrow] * kLog2e : 0.f;
     if (qvalid && h == 0) {
       p.Dbuf[(int64_t)head * p.T + s0 + qrow] = -st.Drow;
-      p.L2buf[(int64_t)head * p.T + s0 + qrow] = st.lse2;
+      p.NLbuf[(int64_t)head * p.T + s0 + qrow] = -p.lse[(int64_t)head * p.T + s0 + qrow] / p.scale;
     }
   }
 #pragma unroll
@@ -326,7 +329,7 @@ __device__ __forceinline__ void mask_half(f32x16& s, int32_t qm, int32_t key, in
 }
 
 template <int D, bool MASK>
-__device__ __forceinline__ void dkdv_block_full(DkvState<D>& st, const char* Qs, const char* dOs, const float* l2s,
+__device__ __forceinline__ void dkdv_block_full(DkvState<D>& st, const char* Qs, const char* dOs, const float* NLs,
                                                 const float* Ds, float c2, int h, const TileReadOffsets& o,
                                                 int32_t qs, int32_t key, int32_t L) {
   constexpr int KS = D / 16;
@@ -336,23 +339,24 @@ __device__ __forceinline__ void dkdv_block_full(DkvState<D>& st, const char* Qs,
   auto offA = [&](int mq, int kk) { return row_off(o, kk) + mq * 32 * 128; };
   // B operand of dV/dK, pair c = ks * (D/32) + dt: column read of rows 32*mq + 16*ks ..
   auto trC = [&](const char* M, int mq, int c) { return col_operand(M + mq * 32 * 128, o, c / (D / 32), c % (D / 32)); };
-  // dp already holds dP - D: its accumulator starts from -D (see below)
-  auto pds = [&](const f32x16& s, const f32x16& dp, const f32x4* l4, bf16x8* pa, bf16x8* da, int i0 = 0,
-                 int i1 = 16) {
+  // s already holds S - lse / scale and dp holds dP - D: their accumulators
+  // start from -lse / scale and -D (see below)
+  auto pds = [&](const f32x16& s, const f32x16& dp, bf16x8* pa, bf16x8* da, int i0 = 0, int i1 = 16) {
 #pragma unroll
     for (int i = i0; i < i1; ++i) {
-      const float pr = fast_exp2(__builtin_fmaf(s[i], c2, -l4[i >> 2][i & 3]));
+      const float pr = fast_exp2(s[i] * c2);
       pa[i >> 3][i & 7] = (bf16)pr;
       da[i >> 3][i & 7] = (bf16)(pr * dp[i]);
     }
   };
-  // -D of this lane's 16 query rows of half mq (register i <-> query
-  // 8 (i / 4) + 4 h + i % 4), the starting value of the dP accumulator
-  auto negD = [&](int mq) {
+  // values of this lane's 16 query rows of half mq (register i <-> query
+  // 8 (i / 4) + 4 h + i % 4): -D and -lse / scale, the starting values of
+  // the dP and S accumulators
+  auto rows16 = [&](const float* vec, int mq) {
     f32x16 r;
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      const f32x4 v = *reinterpret_cast<const f32x4*>(Ds + 32 * mq + 8 * g + 4 * h);
+      const f32x4 v = *reinterpret_cast<const f32x4*>(vec + 32 * mq + 8 * g + 4 * h);
 #pragma unroll
       for (int e = 0; e < 4; ++e) r[4 * g + e] = v[e];
     }
@@ -360,11 +364,10 @@ __device__ __forceinline__ void dkdv_block_full(DkvState<D>& st, const char* Qs,
   };
 
   // ---------------- region 1: A(0)
-  f32x16 s0 = {}, s1 = {};
-  f32x16 dp0 = negD(0);
+  f32x16 s0 = rows16(NLs, 0), s1;
+  f32x16 dp0 = rows16(Ds, 0);
   f32x16 dp1;
   bf16x8 nq[KS], nd[KS];        // A(1) operands
-  f32x4 l4a[4];                 // B(0) row constants
   {
     bf16x8 aq[KS], ad[KS];
 #pragma unroll
@@ -377,9 +380,8 @@ __device__ __forceinline__ void dkdv_block_full(DkvState<D>& st, const char* Qs,
       s0 = mfma32(aq[kk], st.kf[kk], s0);
       dp0 = mfma32(ad[kk], st.vf[kk], dp0);
     }
-#pragma unroll
-    for (int g = 0; g < 4; ++g) l4a[g] = *reinterpret_cast<const f32x4*>(l2s + 8 * g + 4 * h);
-    dp1 = negD(1);
+    s1 = rows16(NLs, 1);
+    dp1 = rows16(Ds, 1);
 #pragma unroll
     for (int kk = 0; kk < PF; ++kk) {
       nq[kk] = ld8(Qs + offA(1, kk));
@@ -398,7 +400,6 @@ __device__ __forceinline__ void dkdv_block_full(DkvState<D>& st, const char* Qs,
   // ---------------- region 2: A(1) + B(0)a
   bf16x8 pa0[2], da0[2];
   bf16x8 cb[PF], cq[PF];        // C(0) operands
-  f32x4 l4b[4];                 // B(1) row constants
   {
 #pragma unroll
     for (int kk = PF; kk < KS; ++kk) {
@@ -411,9 +412,7 @@ __device__ __forceinline__ void dkdv_block_full(DkvState<D>& st, const char* Qs,
       dp1 = mfma32(nd[kk], st.vf[kk], dp1);
     }
     if (MASK) mask_half(s0, qs, key, L, h);
-    pds(s0, dp0, l4a, pa0, da0, 0, 8);
-#pragma unroll
-    for (int g = 0; g < 4; ++g) l4b[g] = *reinterpret_cast<const f32x4*>(l2s + 32 + 8 * g + 4 * h);
+    pds(s0, dp0, pa0, da0, 0, 8);
 #pragma unroll
     for (int c = 0; c < PF; ++c) {
       cb[c] = trC(dOs, 0, c);
@@ -445,7 +444,7 @@ __device__ __forceinline__ void dkdv_block_full(DkvState<D>& st, const char* Qs,
       st.dva[dt] = mfma32(pa0[0], bo[c], st.dva[dt]);
       st.dka[dt] = mfma32(da0[0], bq[c], st.dka[dt]);
     }
-    pds(s0, dp0, l4a, pa0, da0, 8, 16);
+    pds(s0, dp0, pa0, da0, 8, 16);
 #pragma unroll
     for (int c = NC / 2; c < NC; ++c) {
       const int dt = c % (D / 32);
@@ -453,7 +452,7 @@ __device__ __forceinline__ void dkdv_block_full(DkvState<D>& st, const char* Qs,
       st.dka[dt] = mfma32(da0[1], bq[c], st.dka[dt]);
     }
     if (MASK) mask_half(s1, qs + 32, key, L, h);
-    pds(s1, dp1, l4b, pa1, da1, 0, 8);
+    pds(s1, dp1, pa1, da1, 0, 8);
 #pragma unroll
     for (int c = 0; c < PF; ++c) {
       eb[c] = trC(dOs, 1, c);
@@ -482,7 +481,7 @@ __device__ __forceinline__ void dkdv_block_full(DkvState<D>& st, const char* Qs,
       st.dva[dt] = mfma32(pa1[0], bo[c], st.dva[dt]);
       st.dka[dt] = mfma32(da1[0], bq[c], st.dka[dt]);
     }
-    pds(s1, dp1, l4b, pa1, da1, 8, 16);
+    pds(s1, dp1, pa1, da1, 8, 16);
 #pragma unroll
     for (int c = NC / 2; c < NC; ++c) {
       const int dt = c % (D / 32);
@@ -500,17 +499,19 @@ __device__ __forceinline__ void dkdv_block_full(DkvState<D>& st, const char* Qs,
   PSC_SCHED_BARRIER();
 }
 
-// D = 128 needs ~370 registers per wave (K, V operands and dK, dV
-// accumulators of 32 keys), one wave per SIMD; D = 64 fits two.
+// D = 64 only (two waves per SIMD).  At D = 128 the K, V operands and dK, dV
+// accumulators of 32 keys need ~360 registers, one wave per SIMD, and the
+// eight-wave kernel below runs instead.
 template <int D>
-__global__ void __launch_bounds__(kThreads, D == 64 ? 2 : 1) k_bwd_dkdv(BwdParams p) {
+__global__ void __launch_bounds__(kThreads, 2) k_bwd_dkdv(BwdParams p) {
+  static_assert(D == 64, "k_bwd_dkdv8 handles D = 128");
   __shared__ __attribute__((aligned(16))) char Qs0[tile_bytes<D>()];
   __shared__ __attribute__((aligned(16))) char dOs0[tile_bytes<D>()];
   __shared__ __attribute__((aligned(16))) char Qs1[tile_bytes<D>()];
   __shared__ __attribute__((aligned(16))) char dOs1[tile_bytes<D>()];
-  __shared__ __attribute__((aligned(16))) float l2s0[kBMk];
+  __shared__ __attribute__((aligned(16))) float NLs0[kBMk];
   __shared__ __attribute__((aligned(16))) float Ds0[kBMk];
-  __shared__ __attribute__((aligned(16))) float l2s1[kBMk];
+  __shared__ __attribute__((aligned(16))) float NLs1[kBMk];
   __shared__ __attribute__((aligned(16))) float Ds1[kBMk];
 
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, h = l >> 5, lq = l & 31;
@@ -537,15 +538,15 @@ __global__ void __launch_bounds__(kThreads, D == 64 ? 2 : 1) k_bwd_dkdv(BwdParam
   // Blocks run from the document end back to the tile: every tile of a
   // document starts at the same rows, so tiles of one document that run at
   // the same time read the same Q/dO blocks together and L2 serves the rest.
-  auto issue = [&](int32_t t, char* Qs, char* dOs, float* l2s, float* Ds) {
+  auto issue = [&](int32_t t, char* Qs, char* dOs, float* NLs, float* Ds) {
     const int32_t head = kvh * p.group + t / nqb;
     const int32_t qs = kb + (nqb - 1 - t % nqb) * kBMk;
     load_tile<D, kThreads / 64>(p.q + (int64_t)s0 * p.sq + (int64_t)head * D, p.sq, qs, L, qoff, Qs, w, l);
     load_tile<D, kThreads / 64>(p.dout + (int64_t)s0 * p.sdo + (int64_t)head * D, p.sdo, qs, L, ooff, dOs, w, l);
-    if (w == 0) load_vec64_async(p.L2buf + (int64_t)head * p.T + s0, qs, L, l2s, l);
+    if (w == 0) load_vec64_async(p.NLbuf + (int64_t)head * p.T + s0, qs, L, NLs, l);
     if (w == 1) load_vec64_async(p.Dbuf + (int64_t)head * p.T + s0, qs, L, Ds, l);
   };
-  issue(0, Qs0, dOs0, l2s0, Ds0);
+  issue(0, Qs0, dOs0, NLs0, Ds0);
 
   DkvState<D> st;
   {
@@ -568,24 +569,24 @@ __global__ void __launch_bounds__(kThreads, D == 64 ? 2 : 1) k_bwd_dkdv(BwdParam
   for (int32_t t = 0; t < niter; t += 2) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (t + 1 < niter) issue(t + 1, Qs1, dOs1, l2s1, Ds1);
+    if (t + 1 < niter) issue(t + 1, Qs1, dOs1, NLs1, Ds1);
     {
       const int32_t qs = kb + (nqb - 1 - t % nqb) * kBMk;
       if (qs >= wk_lo + 31 && qs + kBMk <= L)
-        dkdv_block_full<D, false>(st, Qs0, dOs0, l2s0, Ds0, c2, h, ro, qs, key, L);
+        dkdv_block_full<D, false>(st, Qs0, dOs0, NLs0, Ds0, c2, h, ro, qs, key, L);
       else if (qs + kBMk - 1 >= wk_lo && wk_lo < L)
-        dkdv_block_full<D, true>(st, Qs0, dOs0, l2s0, Ds0, c2, h, ro, qs, key, L);
+        dkdv_block_full<D, true>(st, Qs0, dOs0, NLs0, Ds0, c2, h, ro, qs, key, L);
     }
     if (t + 1 >= niter) break;
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (t + 2 < niter) issue(t + 2, Qs0, dOs0, l2s0, Ds0);
+    if (t + 2 < niter) issue(t + 2, Qs0, dOs0, NLs0, Ds0);
     {
       const int32_t qs = kb + (nqb - 1 - (t + 1) % nqb) * kBMk;
       if (qs >= wk_lo + 31 && qs + kBMk <= L)
-        dkdv_block_full<D, false>(st, Qs1, dOs1, l2s1, Ds1, c2, h, ro, qs, key, L);
+        dkdv_block_full<D, false>(st, Qs1, dOs1, NLs1, Ds1, c2, h, ro, qs, key, L);
       else if (qs + kBMk - 1 >= wk_lo && wk_lo < L)
-        dkdv_block_full<D, true>(st, Qs1, dOs1, l2s1, Ds1, c2, h, ro, qs, key, L);
+        dkdv_block_full<D, true>(st, Qs1, dOs1, NLs1, Ds1, c2, h, ro, qs, key, L);
     }
   }
 
@@ -603,6 +604,256 @@ __global__ void __launch_bounds__(kThreads, D == 64 ? 2 : 1) k_bwd_dkdv(BwdParam
       }
     }
   }
+}
+
+// ------------------------------------------------- dK/dV, eight waves (D = 128)
+//
+// At D = 128 the four-wave kernel's K, V operands and dK, dV accumulators of
+// 32 keys need ~360 registers, so each SIMD would run one wave with nothing
+// to cover its latencies.  Here K and V of the 128-key tile stay in LDS and
+// every 32-key slice gets two waves, one per 32-query half of each 64-query
+// block: a wave holds its dK, dV accumulators (128 registers) and the scores
+// of one half, fits 256 registers, and each SIMD runs two waves.  The price is
+// LDS traffic: K and V are read again for every block (1.5 instead of 1 KB of
+// operand reads per MFMA).  The two partial sums of a slice meet once per
+// tile, through LDS.
+
+constexpr int kThreads8 = 512;
+
+template <int D>
+struct DkvAcc {
+  f32x16 dka[D / 32], dva[D / 32];
+};
+
+// One 64-query block for one wave of the eight-wave kernel: keys wk_lo .. +31
+// (K, V rows at Kw, Vw in LDS) against the 32 queries qm .. qm + 31 (rows at
+// Qh, dOh; their -lse / scale and -D at NLh, Dh):
+//   A: S = Q K^T, dP = dO V^T - D   (16 MFMAs, row reads of all four operands)
+//   B: P and dS in bf16, as the A operands of C (split in two 16-query slices)
+//   C: dV += P^T dO, dK += dS^T Q    (16 MFMAs, column reads of dO and Q)
+// The second slice of B runs between the MFMAs of C's first slice.
+template <int D, bool MASK>
+__device__ __forceinline__ void dkdv_half(DkvAcc<D>& st, const char* Qh, const char* dOh, const char* Kw,
+                                          const char* Vw, const float* NLh, const float* Dh, float c2, int h,
+                                          const TileReadOffsets& o, int32_t qm, int32_t key, int32_t L) {
+  constexpr int KS = D / 16;
+  constexpr int DT = D / 32;
+  // the accumulators start from -lse / scale and -D of the lane's query rows
+  // (register i <-> query qm + 8 (i / 4) + 4 h + i % 4)
+  f32x16 s, dp;
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const f32x4 a = *reinterpret_cast<const f32x4*>(NLh + 8 * g + 4 * h);
+    const f32x4 v = *reinterpret_cast<const f32x4*>(Dh + 8 * g + 4 * h);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      s[4 * g + e] = a[e];
+      dp[4 * g + e] = v[e];
+    }
+  }
+  // A: both chains advance together, operands read PF k-steps ahead
+  {
+    constexpr int PF = 3;
+    bf16x8 aq[KS], ak[KS], ad[KS], av[KS];
+    auto rd = [&](int kk) {
+      aq[kk] = ld8(Qh + row_off(o, kk));
+      ak[kk] = ld8(Kw + row_off(o, kk));
+      ad[kk] = ld8(dOh + row_off(o, kk));
+      av[kk] = ld8(Vw + row_off(o, kk));
+    };
+#pragma unroll
+    for (int kk = 0; kk < PF; ++kk) rd(kk);
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+      if (kk + PF < KS) rd(kk + PF);
+      s = mfma32(aq[kk], ak[kk], s);
+      dp = mfma32(ad[kk], av[kk], dp);
+    }
+    PSC_SCHED_DS_READ(4 * PF + 4);
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+      PSC_SCHED_MFMA(2);
+      if (kk + PF + 1 < KS) PSC_SCHED_DS_READ(4);
+    }
+  }
+  // operands of C's first slice, read while A drains
+  // (pair ks, dt covers queries 16 ks .. +15 and columns 32 dt .. +31)
+  bf16x8 bo[DT], bq[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) {
+    bo[dt] = col_operand(dOh, o, 0, dt);
+    bq[dt] = col_operand(Qh, o, 0, dt);
+  }
+  if (MASK) mask_half(s, qm, key, L, h);
+  bf16x8 pa[2], da[2];
+  auto pds = [&](int i0, int i1) {
+#pragma unroll
+    for (int i = i0; i < i1; ++i) {
+      const float pr = fast_exp2(s[i] * c2);
+      pa[i >> 3][i & 7] = (bf16)pr;
+      da[i >> 3][i & 7] = (bf16)(pr * dp[i]);
+    }
+  };
+  pds(0, 8);
+  // C: first slice, with B's second slice and the second slice's operands
+  // between its MFMAs
+  bf16x8 bo1[DT], bq1[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) {
+    bo1[dt] = col_operand(dOh, o, 1, dt);
+    bq1[dt] = col_operand(Qh, o, 1, dt);
+  }
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) {
+    st.dva[dt] = mfma32(pa[0], bo[dt], st.dva[dt]);
+    st.dka[dt] = mfma32(da[0], bq[dt], st.dka[dt]);
+  }
+  pds(8, 16);
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) {
+    st.dva[dt] = mfma32(pa[1], bo1[dt], st.dva[dt]);
+    st.dka[dt] = mfma32(da[1], bq1[dt], st.dka[dt]);
+  }
+}
+
+// Wave w takes keys kb + 32 (w % 4) .. +31 and the query half w / 4 of every
+// block; the two waves of a key slice add their partial dK, dV at the end.
+template <int D>
+__global__ void __launch_bounds__(kThreads8, 1) k_bwd_dkdv8(BwdParams p) {
+  constexpr int TB = tile_bytes<D>();
+  constexpr int NW = kThreads8 / 64;
+  constexpr int DT = D / 32;
+  // Q, dO stage 0 | Q, dO stage 1 | K (2 tiles) | V (2 tiles) | lse, -D x 2:
+  // the four stage tiles lie within the 64 KB that a ds_read offset field
+  // reaches from one base, and so do K and V from another
+  __shared__ __attribute__((aligned(16))) char sm[8 * TB + 4 * kBMk * sizeof(float)];
+  char* const Qs0 = sm;
+  char* const dOs0 = sm + TB;
+  char* const Qs1 = sm + 2 * TB;
+  char* const dOs1 = sm + 3 * TB;
+  char* const Kt = sm + 4 * TB;
+  char* const Vt = sm + 6 * TB;
+  float* const NLs0 = reinterpret_cast<float*>(sm + 8 * TB);
+  float* const Ds0 = NLs0 + kBMk;
+  float* const NLs1 = Ds0 + kBMk;
+  float* const Ds1 = NLs1 + kBMk;
+
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, h = l >> 5, lq = l & 31;
+  const int ks = w & 3, qh = w >> 2;
+  const uint32_t item = blockIdx.x / (uint32_t)p.hkv, kvh = blockIdx.x % (uint32_t)p.hkv;
+  // item < cap (the grid is cap work-groups per head), so the entry is read
+  // together with the count and used only once the count admits it.  Segment
+  // bounds come clamped to [0, T] from the schedule.
+  const int4 it = *reinterpret_cast<const int4*>(p.items + 4 * item);
+  if ((int32_t)item >= *p.n_items) return;
+  const int32_t s0 = it.x, L = it.y, tile = it.z;
+  const int32_t kb = tile * kBKV;
+  if (kb >= L) return;
+  const int32_t wk_lo = kb + 32 * ks;
+  const int32_t key = wk_lo + lq;  // this lane's key (S layout: lane <-> key)
+  const int32_t nqb = (L - kb + kBMk - 1) / kBMk;
+  const int32_t niter = p.group * nqb;
+
+  uint32_t qoff[D / 8 / NW], ooff[D / 8 / NW];
+  tile_offsets<D, NW>(p.sq, w, l, qoff);
+  tile_offsets<D, NW>(p.sdo, w, l, ooff);
+  {
+    uint32_t koff[D / 8 / NW], voff[D / 8 / NW];
+    tile_offsets<D, NW>(p.sk, w, l, koff);
+    tile_offsets<D, NW>(p.sv, w, l, voff);
+    const bf16* Kp = p.k + (int64_t)s0 * p.sk + (int64_t)kvh * D;
+    const bf16* Vp = p.v + (int64_t)s0 * p.sv + (int64_t)kvh * D;
+    load_tile<D, NW>(Kp, p.sk, kb, L, koff, Kt, w, l);
+    load_tile<D, NW>(Kp, p.sk, kb + kTileRows, L, koff, Kt + TB, w, l);
+    load_tile<D, NW>(Vp, p.sv, kb, L, voff, Vt, w, l);
+    load_tile<D, NW>(Vp, p.sv, kb + kTileRows, L, voff, Vt + TB, w, l);
+  }
+  // iteration t: query head kvh*G + t / nqb, query block kb + (nqb - 1 - t % nqb) * 64,
+  // from the document end back to the tile (as in the four-wave kernel)
+  auto issue = [&](int32_t t, char* Qs, char* dOs, float* NLs, float* Ds) {
+    const int32_t head = kvh * p.group + t / nqb;
+    const int32_t qs = kb + (nqb - 1 - t % nqb) * kBMk;
+    load_tile<D, NW>(p.q + (int64_t)s0 * p.sq + (int64_t)head * D, p.sq, qs, L, qoff, Qs, w, l);
+    load_tile<D, NW>(p.dout + (int64_t)s0 * p.sdo + (int64_t)head * D, p.sdo, qs, L, ooff, dOs, w, l);
+    if (w == 0) load_vec64_async(p.NLbuf + (int64_t)head * p.T + s0, qs, L, NLs, l);
+    if (w == 1) load_vec64_async(p.Dbuf + (int64_t)head * p.T + s0, qs, L, Ds, l);
+  };
+  issue(0, Qs0, dOs0, NLs0, Ds0);
+
+  DkvAcc<D> st;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) {
+    st.dka[dt] = f32x16{};
+    st.dva[dt] = f32x16{};
+  }
+  const float c2 = p.scale_log2;
+  const TileReadOffsets ro = tile_read_offsets(h, lq, l);
+  // rows lq and 32 + lq share the swizzle, so a 32-row slice is a fixed offset
+  const char* const Kw = Kt + (ks >> 1) * TB + (ks & 1) * 32 * 128;
+  const char* const Vw = Vt + (ks >> 1) * TB + (ks & 1) * 32 * 128;
+  auto block = [&](int32_t t, const char* Qs, const char* dOs, const float* NLs, const float* Ds) {
+    const int32_t qm = kb + (nqb - 1 - t % nqb) * kBMk + 32 * qh;
+    const char* Qh = Qs + qh * 32 * 128;
+    const char* dOh = dOs + qh * 32 * 128;
+    if (qm >= wk_lo + 31 && qm + 32 <= L)
+      dkdv_half<D, false>(st, Qh, dOh, Kw, Vw, NLs + 32 * qh, Ds + 32 * qh, c2, h, ro, qm, key, L);
+    else if (qm + 31 >= wk_lo && qm < L && wk_lo < L)
+      dkdv_half<D, true>(st, Qh, dOh, Kw, Vw, NLs + 32 * qh, Ds + 32 * qh, c2, h, ro, qm, key, L);
+  };
+  for (int32_t t = 0; t < niter; t += 2) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (t + 1 < niter) issue(t + 1, Qs1, dOs1, NLs1, Ds1);
+    block(t, Qs0, dOs0, NLs0, Ds0);
+    if (t + 1 >= niter) break;
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (t + 2 < niter) issue(t + 2, Qs0, dOs0, NLs0, Ds0);
+    block(t + 1, Qs1, dOs1, NLs1, Ds1);
+  }
+
+  // The two waves of a key slice meet: the query-half-1 wave hands its dK over
+  // and the half-0 wave its dV (regions of 16 KB, lane-major 16-byte pieces),
+  // then each adds its partner's part to the one it keeps and stores it.
+  __syncthreads();  // every wave is done with the tiles
+  f32x4* const red = reinterpret_cast<f32x4*>(sm);
+  constexpr int kPieces = DT * 4 * 64;  // f32x4 pieces per wave
+  auto give = [&](const f32x16* x) {
+    f32x4* mine = red + (2 * ks + qh) * kPieces;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        mine[(4 * dt + g) * 64 + l] = f32x4{x[dt][4 * g], x[dt][4 * g + 1], x[dt][4 * g + 2], x[dt][4 * g + 3]};
+    }
+  };
+  // add the partner's part and store (C layout: key = wk_lo + 8*(i/4) + 4*h + i%4, d = 32*dt + lq)
+  auto finish = [&](f32x16* x, float* outp, float mul) {
+    const f32x4* theirs = red + (2 * ks + (qh ^ 1)) * kPieces;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 y = theirs[(4 * dt + g) * 64 + l];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[dt][4 * g + e] += y[e];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int32_t kr = wk_lo + 8 * (i >> 2) + 4 * h + (i & 3);
+      if (kr < L) {
+        float* r = outp + ((int64_t)(s0 + kr) * p.hkv + kvh) * D;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) r[32 * dt + lq] = x[dt][i] * mul;
+      }
+    }
+  };
+  if (qh) give(st.dka);
+  else give(st.dva);
+  __syncthreads();
+  if (qh) finish(st.dva, p.dv, 1.f);
+  else finish(st.dka, p.dk, p.scale);
 }
 
 }  // namespace
@@ -627,7 +878,7 @@ hipError_t launch_attn_bwd_bf16(const AttnBwdArgs& a, hipStream_t stream) {
   char* ws = static_cast<char*>(a.workspace);
   float* Dbuf = reinterpret_cast<float*>(ws);
   ws += vec_bytes(d);
-  float* L2buf = reinterpret_cast<float*>(ws);
+  float* NLbuf = reinterpret_cast<float*>(ws);
   ws += vec_bytes(d);
   const int hp = dq_heads_per_wg(d);
   TileSchedule sq = schedule_carve(ws, d.T, d.n_seg, d.max_seqlen, kBQ / hp, kBNq);
@@ -642,7 +893,7 @@ hipError_t launch_attn_bwd_bf16(const AttnBwdArgs& a, hipStream_t stream) {
   p.dout = static_cast<const bf16*>(a.dout);
   p.lse = a.lse;
   p.Dbuf = Dbuf;
-  p.L2buf = L2buf;
+  p.NLbuf = NLbuf;
   p.dq = a.dq;
   p.dk = a.dk;
   p.dv = a.dv;
@@ -660,7 +911,7 @@ hipError_t launch_attn_bwd_bf16(const AttnBwdArgs& a, hipStream_t stream) {
   p.scale_log2 = d.scale * kLog2e;
   if (d.T == 0) return hipSuccess;
 
-  // dQ first: it also produces D and lse * log2 e, which dK/dV reads.
+  // dQ first: it also produces -D and -lse / scale, which dK/dV reads.
   hipError_t e = launch_schedule(a.cu, d.n_seg, (int32_t)d.T, kBQ / hp, kBNq, false, sq, stream);
   if (e != hipSuccess) return e;
   p.items = sq.items;
@@ -687,7 +938,7 @@ hipError_t launch_attn_bwd_bf16(const AttnBwdArgs& a, hipStream_t stream) {
   {
     ScopedKernelTimer timed(kTimeBwdDkdv, stream);
     if (d.d == 128)
-      k_bwd_dkdv<128><<<grid_kv, kThreads, 0, stream>>>(p);
+      k_bwd_dkdv8<128><<<grid_kv, kThreads8, 0, stream>>>(p);
     else
       k_bwd_dkdv<64><<<grid_kv, kThreads, 0, stream>>>(p);
   }
