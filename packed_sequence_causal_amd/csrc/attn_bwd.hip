@@ -297,9 +297,9 @@ struct DkvState {
   f32x16 dka[D / 32], dva[D / 32];
 };
 
-// One 64-query block of the dK/dV loop for one wave (keys wk_lo .. +31, this
-// lane's key `key`), software-pipelined inside the wave (at one wave per SIMD
-// nothing else fills the matrix core while a wave waits).  Blocks on the
+// One 64-query block of the four-wave dK/dV loop for one wave (keys wk_lo ..
+// +31, this lane's key `key`), software-pipelined inside the wave (a wave's own
+// instruction stream has to hide most of its latencies).  Blocks on the
 // diagonal or at the document end (MASK) take the same schedule with the
 // mask applied to S just before B; a half whose queries all precede the
 // wave's keys is computed and then fully masked (cheaper than a separate,
