@@ -45,9 +45,9 @@ KERNEL_SOURCES = {
 }
 MEASURED_TRAFFIC = {
     # (kernel, workload): (sources sha256 prefix, read bytes, write bytes)
-    ("attn_fwd", "lognormal_32k"): ("17033b393f969993", 2.0 * 420238.1 * 1024, 1.0 * 533377.5 * 1024),
-    ("attn_bwd_dkdv", "lognormal_32k"): ("5cb096c7b1a87504", 2.0 * 4193579.1 * 1024, 1.0 * 532863.6 * 1024),
-    ("attn_bwd_dq", "lognormal_32k"): ("5cb096c7b1a87504", 2.0 * 967303.7 * 1024, 1.0 * 1065944.6 * 1024),
+    ("attn_fwd", "lognormal_32k"): ("17033b393f969993", 2.0 * 420369.4 * 1024, 1.0 * 533396.8 * 1024),
+    ("attn_bwd_dkdv", "lognormal_32k"): ("0171924ac3e7b751", 2.0 * 4199159.2 * 1024, 1.0 * 532863.5 * 1024),
+    ("attn_bwd_dq", "lognormal_32k"): ("0171924ac3e7b751", 2.0 * 967306.0 * 1024, 1.0 * 1065907.8 * 1024),
 }
 
 
