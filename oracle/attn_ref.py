@@ -184,36 +184,50 @@ def attn_rows_dq(q, k, v, do, cu_seqlens, rows, heads, softmax_scale=None):
     return np.array(out)
 
 
-def attn_bwd_keys(q, k, v, do, cu_seqlens, seg, key_lo, kv_heads, softmax_scale=None, block=512):
-    """dk, dv for the keys [key_lo, e) of segment ``seg`` = [s, e) and the
-    listed key/value heads only.
+def attn_bwd_keys(q, k, v, do, cu_seqlens, seg, key_lo, kv_heads, softmax_scale=None, block=512, key_hi=None):
+    """dk, dv for the keys [key_lo, key_hi) of segment ``seg`` = [s, e) and the
+    listed key/value heads only (key_hi defaults to e).
 
-    dk_j and dv_j need every query row i >= j of the document; each such row's
-    lse_i and D_i come from its full causal prefix, so rows [key_lo, e) are
-    computed in full and only the key columns >= key_lo are accumulated.
-    Returns arrays [e - key_lo, len(kv_heads), D].
+    dk_j and dv_j need every query row i >= j of the document, and each such
+    row's lse_i and D_i come from its full causal prefix: for every row block,
+    the scores against the whole prefix give lse_i and o_i = sum_j P_ij v_j,
+    D_i = <dO_i, o_i>, and then only the key columns [key_lo, key_hi) form P,
+    dP and dS and are accumulated.  fp64 throughout (torch CPU tensors, whose
+    exp and matmul use every core; the arithmetic is the plain definition).
+    Returns arrays [key_hi - key_lo, len(kv_heads), D].
     """
+    import torch
+
     Hq, D = q.shape[1], q.shape[2]
     G = Hq // k.shape[1]
     scale = _scale(D, softmax_scale)
     cu = [int(c) for c in np.asarray(cu_seqlens).reshape(-1)]
     s, e = cu[seg], cu[seg + 1]
-    n = e - key_lo
-    dk = np.zeros((n, len(kv_heads), D))
-    dv = np.zeros((n, len(kv_heads), D))
+    key_hi = e if key_hi is None else min(int(key_hi), e)
+    assert s <= key_lo < key_hi, (s, key_lo, key_hi)
+    n = key_hi - key_lo
+    c0, c1 = key_lo - s, key_hi - s
+    t64 = lambda x: torch.from_numpy(np.ascontiguousarray(x))
+    dk = torch.zeros((n, len(kv_heads), D), dtype=torch.float64)
+    dv = torch.zeros((n, len(kv_heads), D), dtype=torch.float64)
     for gi, g in enumerate(kv_heads):
-        K, V = _slice64(k, slice(s, e), g), _slice64(v, slice(s, e), g)
+        K, V = t64(_slice64(k, slice(s, e), g)), t64(_slice64(v, slice(s, e), g))
         for h in range(g * G, (g + 1) * G):
-            Q, dO = _slice64(q, slice(s, e), h), _slice64(do, slice(s, e), h)
-            for i0 in range(key_lo - s, e - s, block):
+            Q, dO = t64(_slice64(q, slice(s, e), h)), t64(_slice64(do, slice(s, e), h))
+            for i0 in range(c0, e - s, block):
                 i1 = min(i0 + block, e - s)
-                S = _causal_block_scores(Q[i0:i1], K[:i1], i0, scale)
-                m = S.max(axis=1, keepdims=True)
-                P = np.exp(S - m)
-                P /= P.sum(axis=1, keepdims=True)
-                dP = dO[i0:i1] @ V[:i1].T
-                dS = P * (dP - (P * dP).sum(axis=1, keepdims=True))
-                c0 = key_lo - s
-                dk[: i1 - c0, gi] += scale * (dS[:, c0:].T @ Q[i0:i1])
-                dv[: i1 - c0, gi] += P[:, c0:].T @ dO[i0:i1]
-    return dk, dv
+                S = scale * (Q[i0:i1] @ K[:i1].T)
+                rows = torch.arange(i0, i1)[:, None]
+                S.masked_fill_(torch.arange(i1)[None, :] > rows, -math.inf)
+                m = S.max(dim=1, keepdim=True).values
+                E = torch.exp(S - m)
+                lsum = E.sum(dim=1, keepdim=True)
+                o = (E @ V[:i1]) / lsum                       # o_i
+                Drow = (dO[i0:i1] * o).sum(dim=1, keepdim=True)  # D_i = <dO_i, o_i>
+                ce = min(c1, i1)  # rows i0.. see keys up to i1 - 1 only
+                P = E[:, c0:ce] / lsum
+                dP = dO[i0:i1] @ V[c0:ce].T
+                dS = P * (dP - Drow)
+                dk[: ce - c0, gi] += scale * (dS.T @ Q[i0:i1])
+                dv[: ce - c0, gi] += P.T @ dO[i0:i1]
+    return dk.numpy(), dv.numpy()

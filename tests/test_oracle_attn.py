@@ -253,3 +253,24 @@ def test_key_tail_gradients_match_full_oracle():
         np.testing.assert_allclose(tk[:, 0], dk[key_lo:e, 1], atol=1e-13)
         np.testing.assert_allclose(tk[:, 1], dk[key_lo:e, 0], atol=1e-13)
         np.testing.assert_allclose(tv[:, 0], dv[key_lo:e, 1], atol=1e-13)
+
+
+def test_key_window_gradients_match_full_oracle():
+    # a window [key_lo, key_hi) anywhere in a document, the head of a document
+    # included: only those key columns accumulate, every later query row
+    # contributes, and rows before key_lo do not
+    T = 260
+    cu = np.array([0, 37, 200, 260], dtype=np.int32)
+    q, k, v, do = _inputs(T, 4, 2, 16, 22)
+    _, dk, dv = attn_ref.attn_bwd(q, k, v, do, cu)
+    for seg, key_lo, key_hi in [(1, 37, 37 + 16), (1, 37, 38), (1, 100, 131), (2, 200, 259), (0, 0, 37)]:
+        for block in (7, 512):
+            tk, tv = attn_ref.attn_bwd_keys(q, k, v, do, cu, seg, key_lo, [1, 0], block=block, key_hi=key_hi)
+            assert tk.shape == (key_hi - key_lo, 2, 16)
+            np.testing.assert_allclose(tk[:, 0], dk[key_lo:key_hi, 1], atol=1e-13)
+            np.testing.assert_allclose(tk[:, 1], dk[key_lo:key_hi, 0], atol=1e-13)
+            np.testing.assert_allclose(tv[:, 0], dv[key_lo:key_hi, 1], atol=1e-13)
+            np.testing.assert_allclose(tv[:, 1], dv[key_lo:key_hi, 0], atol=1e-13)
+    # a window past the document end is cut at the end
+    tk, _ = attn_ref.attn_bwd_keys(q, k, v, do, cu, 0, 30, [0], key_hi=1000)
+    np.testing.assert_allclose(tk[:, 0], dk[30:37, 0], atol=1e-13)
