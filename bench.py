@@ -29,9 +29,12 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
+import workloads  # noqa: E402  (seeded synthetic inputs; no torch at import)
+
 METRIC = "varlen causal attn fwd+bwd TFLOP/s (in-doc FLOPs) & % MFMA peak, 1 GPU"
 PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 4096 dense bf16 FLOP/clk x 2.4 GHz (published 2.5 PFLOP/s)
 PEAK_HBM_GBS = 8000.0
+BF16_WORKLOADS = ["lognormal_32k", "uniform_8k", "seqpar_share_128k", "skewed_32k"]
 
 
 # HBM bytes per launch measured with rocprofv3 FETCH_SIZE / WRITE_SIZE (each
@@ -77,6 +80,8 @@ def parse():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the CPU oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-other-workloads", action="store_true",
+                    help="time only --workload (by default the line also carries every other bf16 workload)")
     ap.add_argument("--doc-sweep", action="store_true",
                     help="time each 32K document layout with its document mask and as one whole-row causal "
                          "segment (same kernels); one JSON line per layout")
@@ -106,6 +111,27 @@ def real_segments(w, cu):
     if w.attn_is_pad is not None:
         return ~np.asarray(w.attn_is_pad, dtype=bool)
     return np.ones(len(cu) - 1, dtype=bool)
+
+
+def cpu_model():
+    """The host CPU's model name, as lscpu reports it (else /proc/cpuinfo)."""
+    import subprocess
+
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            if line.startswith("Model name:"):
+                return line.split(":", 1)[1].strip()
+    except (OSError, subprocess.SubprocessError):
+        pass
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def cpu_baseline(w, q, k, v, do, cu, real, budget_s):
@@ -146,6 +172,8 @@ def cpu_baseline(w, q, k, v, do, cu, real, budget_s):
         "value": flops / dt / 1e12,
         "unit": "TFLOP/s",
         "cores": int(threads),
+        "cpu_model": cpu_model(),
+        "host_cpus": len(os.sched_getaffinity(0)),
         "kind": "oracle",
         "sample": f"fp64 NumPy oracle, fwd{'+bwd' if a.backward else ''} of the first {docs} documents "
                   f"(one key/value group of {a.hq // a.hkv} query heads each), {flops:.3e} in-doc FLOP "
@@ -283,30 +311,13 @@ def doc_sweep(args):
         print(json.dumps(line), flush=True)
 
 
-def main():
-    args = parse()
-    world = int(os.environ.get("WORLD_SIZE", "1"))
-    if args.gpus != 1 or world != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
-                          "n_gpus": args.gpus}))
-        sys.exit(2)
-    if args.calibrate_copy_mib:
-        calibrate_copy(args.calibrate_copy_mib)
-        return
-    if args.doc_sweep:
-        doc_sweep(args)
-        return
-
-    import numpy as np
-    import torch
-
-    import packed_sequence_causal_amd as psc
-    import workloads
-
+def measure(w, args, steps, warmup, torch, np, psc):
+    """Times `steps` steps (pack + fwd [+ bwd]) of workload w after `warmup`
+    untimed ones, with the library's per-kernel HIP-event timing on.
+    Returns (summary dict, context for the extra rows)."""
     dev = torch.device("cuda:0")
-    w = workloads.make(args.workload, args.seed)
     a = w.attn
-    mode = psc.PACK if w.pack.mode == workloads.BUILD_PACK else psc.UNPACK
+    mode = psc.PACK if w.pack.mode == "pack" else psc.UNPACK
 
     toks = torch.from_numpy(w.pack.tokens).to(dev)
     offs = torch.from_numpy(w.pack.doc_offsets).to(dev)
@@ -331,19 +342,18 @@ def main():
 
     q, k, v, do = workloads.qkv_do(T, a.hq, a.hkv, a.head_dim, seed=args.seed, dtype=a.dtype)
     qd, kd, vd, dod = q.to(dev), k.to(dev), v.to(dev), do.to(dev)
+    dt = psc.BF16 if a.dtype == "bf16" else psc.F32
     o, lse = psc.varlen_attn_fwd(qd, kd, vd, cu, max_seqlen, n_segments=n_seg)
-    ws_f = torch.empty(psc.varlen_attn_workspace(0, psc.BF16 if a.dtype == "bf16" else psc.F32, T, n_seg,
-                                                 max_seqlen, a.hq, a.hkv, a.head_dim), dtype=torch.uint8,
-                       device=dev)
+    ws_f = torch.empty(psc.varlen_attn_workspace(0, dt, T, n_seg, max_seqlen, a.hq, a.hkv, a.head_dim),
+                       dtype=torch.uint8, device=dev)
     grads = ws_b = None
     if a.backward:
         grads = psc.varlen_attn_bwd(qd, kd, vd, o, dod, lse, cu, max_seqlen, n_segments=n_seg)
-        ws_b = torch.empty(psc.varlen_attn_workspace(1, psc.BF16 if a.dtype == "bf16" else psc.F32, T, n_seg,
-                                                     max_seqlen, a.hq, a.hkv, a.head_dim), dtype=torch.uint8,
-                           device=dev)
+        ws_b = torch.empty(psc.varlen_attn_workspace(1, dt, T, n_seg, max_seqlen, a.hq, a.hkv, a.head_dim),
+                           dtype=torch.uint8, device=dev)
     pk_ws = pk["_workspace"]
 
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
 
     def step(e=None):
         if e:
@@ -360,7 +370,7 @@ def main():
         if e:
             e[3].record()
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
     psc.timing_reset()
@@ -368,21 +378,63 @@ def main():
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0.record()
-    for i in range(args.steps):
+    for i in range(steps):
         step(ev[i])
     t1.record()
     torch.cuda.synchronize()
     psc.timing_enable(False)
     kt = psc.timing_read()
-    ms = t0.elapsed_time(t1) / args.steps
-    pack_ms = float(np.median([e[0].elapsed_time(e[1]) for e in ev]))
+    ms = t0.elapsed_time(t1) / steps
     fwd_all = [e[1].elapsed_time(e[2]) for e in ev]
     bwd_all = [e[2].elapsed_time(e[3]) for e in ev]
     fwd_ms = float(np.median(fwd_all))
     bwd_ms = float(np.median(bwd_all)) if a.backward else 0.0
+    value = (fwd_flops + bwd_flops) / (ms * 1e-3) / 1e12
+    summary = {
+        "workload": w.name, "tokens": T, "real_tokens": real_tokens, "segments": n_seg, "max_seqlen": max_seqlen,
+        "hq": a.hq, "hkv": a.hkv, "head_dim": a.head_dim, "dtype": a.dtype,
+        "passes": "pack+fwd+bwd" if a.backward else "pack+fwd", "steps": steps, "warmup": warmup,
+        "ms_per_step": round(ms, 4), "tflops": round(value, 2),
+        "pct_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "tokens_per_s": round(real_tokens / (ms * 1e-3), 1),
+        "pack_ms": round(float(np.median([e[0].elapsed_time(e[1]) for e in ev])), 4),
+        "fwd": {"ms": round(fwd_ms, 4), "min_ms": round(float(min(fwd_all)), 4),
+                "tflops": round(fwd_flops / (fwd_ms * 1e-3) / 1e12, 2),
+                "pct_peak": round(100 * fwd_flops / (fwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2)},
+        "kernels_ms_per_step": {n: round(t / steps, 4) for n, (t, c) in kt.items() if c},
+    }
+    if a.backward:
+        summary["bwd"] = {"ms": round(bwd_ms, 4), "min_ms": round(float(min(bwd_all)), 4),
+                          "tflops": round(bwd_flops / (bwd_ms * 1e-3) / 1e12, 2),
+                          "pct_peak": round(100 * bwd_flops / (bwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2)}
+    ctx = dict(q=q, k=k, v=v, do=do, qd=qd, kd=kd, pk=pk, cu_h=cu_h, real=real, kt=kt, ms=ms, value=value,
+               fwd_flops=fwd_flops, bwd_flops=bwd_flops)
+    return summary, ctx
 
-    total_flops = fwd_flops + bwd_flops
-    value = total_flops / (ms * 1e-3) / 1e12
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+    if args.calibrate_copy_mib:
+        calibrate_copy(args.calibrate_copy_mib)
+        return
+    if args.doc_sweep:
+        doc_sweep(args)
+        return
+
+    import numpy as np
+    import torch
+
+    import packed_sequence_causal_amd as psc
+
+    w = workloads.make(args.workload, args.seed)
+    a = w.attn
+    summ, ctx = measure(w, args, args.steps, args.warmup, torch, np, psc)
+    kt, fwd_flops = ctx["kt"], ctx["fwd_flops"]
 
     # dominant kernel and its algorithmic work per launch: forward = the two
     # in-document products; dK/dV = S, dP, dV, dK (2.0x forward); dQ = the dQ
@@ -401,39 +453,52 @@ def main():
 
     result = {
         "metric": METRIC,
-        "value": round(value, 2),
+        "value": summ["tflops"],
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms, 4),
+        "ms_per_step": summ["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": a.dtype,
         "data": "synthetic",
-        "config": {"workload": w.name, "tokens": T, "real_tokens": real_tokens, "segments": n_seg,
-                   "max_seqlen": max_seqlen, "hq": a.hq, "hkv": a.hkv, "head_dim": a.head_dim,
+        "config": {"workload": w.name, "tokens": summ["tokens"], "real_tokens": summ["real_tokens"],
+                   "segments": summ["segments"], "max_seqlen": summ["max_seqlen"], "hq": a.hq, "hkv": a.hkv,
+                   "head_dim": a.head_dim,
                    "packer": f"{w.pack.mode}(micro_bsz={w.pack.micro_bsz}, seq_len={w.pack.seq_len}), "
                              f"{len(w.pack.docs)} docs",
-                   "passes": "pack+fwd+bwd" if a.backward else "pack+fwd", "seed": args.seed},
-        "pct_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
-        "tokens_per_s": round(real_tokens / (ms * 1e-3), 1),
-        "pack_ms": round(pack_ms, 4),
-        "fwd": {"ms": round(fwd_ms, 4), "min_ms": round(float(min(fwd_all)), 4),
-                "tflops": round(fwd_flops / (fwd_ms * 1e-3) / 1e12, 2),
-                "pct_peak": round(100 * fwd_flops / (fwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2)},
-        "kernels_ms_per_step": {n: round(t / args.steps, 4) for n, (t, c) in kt.items() if c},
+                   "passes": summ["passes"], "seed": args.seed},
+        "pct_peak": summ["pct_peak"],
+        "tokens_per_s": summ["tokens_per_s"],
+        "pack_ms": summ["pack_ms"],
+        "fwd": summ["fwd"],
+        "kernels_ms_per_step": summ["kernels_ms_per_step"],
         "roofline": roofline,
     }
     if a.backward:
-        result["bwd"] = {"ms": round(bwd_ms, 4), "min_ms": round(float(min(bwd_all)), 4),
-                         "tflops": round(bwd_flops / (bwd_ms * 1e-3) / 1e12, 2),
-                         "pct_peak": round(100 * bwd_flops / (bwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2)}
-    result["rope"] = rope_rate(psc, torch, np, qd, kd, pk, w, args)
-    result["data_steps"] = data_steps_rate(psc, torch, np, pk, w)
+        result["bwd"] = summ["bwd"]
+    result["rope"] = rope_rate(psc, torch, np, ctx["qd"], ctx["kd"], ctx["pk"], w, args)
+    result["data_steps"] = data_steps_rate(psc, torch, np, ctx["pk"], w)
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w, q, k, v, do, cu_h, real, args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(w, ctx["q"], ctx["k"], ctx["v"], ctx["do"], ctx["cu_h"], ctx["real"],
+                                              args.cpu_seconds)
+    # the other bf16 workloads, same step, fewer timed steps: their own lines
+    # in one object so that every workload's rate is in the driver's record
+    if not args.no_other_workloads:
+        del ctx
+        others = {}
+        for name in BF16_WORKLOADS:
+            if name == w.name:
+                continue
+            torch.cuda.empty_cache()
+            wo = workloads.make(name, args.seed)
+            s_o, _ = measure(wo, args, min(args.steps, 10), min(args.warmup, 3), torch, np, psc)
+            others[name] = s_o
+            print(f"# {name}: {s_o['ms_per_step']} ms/step, fwd {s_o['fwd']['pct_peak']} %"
+                  + (f", bwd {s_o['bwd']['pct_peak']} %" if "bwd" in s_o else ""), file=sys.stderr, flush=True)
+        result["workloads"] = others
     print(json.dumps(result), flush=True)
 
 

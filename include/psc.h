@@ -207,12 +207,28 @@ int psc_rope(int dtype, void* q, int64_t q_tok_stride, int32_t hq, void* k, int6
  * tok_stride at most 2^25 elements (a 64-row tile's byte offsets fit 32 bits);
  * otherwise PSC_ERR_INVALID.
  * cu_seqlens int32 [n_segments + 1]: 0 = c_0 < c_1 < ... < c_n = T (strictly
- * increasing; precondition, not checked on the device).  max_seqlen >= the
- * longest segment (used for scratch sizing only; never for addressing).
+ * increasing).  This is a precondition: release builds do not check it (every
+ * access is still clamped to [0, T), so a bad array gives wrong results, never
+ * an access outside the tensors); builds with debug checks (psc_debug_checks()
+ * returns 1) run psc_check_cu_seqlens first, wait for it, and return
+ * PSC_ERR_INVALID before any launch when it fails.  max_seqlen >= the longest
+ * segment (used for scratch sizing only; never for addressing).
  * Query head h reads key/value head h / (hq/hkv) (grouped-query attention:
  * InternEvo "数据加载与流程", section "ISP并行模式下数据流程", qkv split).
  * softmax_scale <= 0 selects 1/sqrt(D).
- * head_dim: PSC_BF16 supports 64 and 128; PSC_F32 supports 32, 64, 128.
+ * head_dim: 32, 64 or 128 for both dtypes (PSC_BF16 runs head_dim 32 in its
+ * 64-column kernels with the extra columns zeroed; results are those of the
+ * 32 columns).
+ * Accuracy of PSC_BF16 (P and dS are rounded to bf16 before their products):
+ * against fp64 attention of the same bf16 inputs of unit scale, O, lse, dQ,
+ * dK and dV were measured within max-abs 2e-2 and rel-L2 5e-3 for
+ * softmax_scale up to 1.5/sqrt(D) and up to 4 query heads per key/value head
+ * at head_dim 64 and 128 (up to 2 at head_dim 32).  Beyond that the max-abs
+ * error of the gradients grows while rel-L2 stays near 2e-3: softmax_scale
+ * 1.75/sqrt(D) gave dK 3.1e-2 and 0.2 at D = 128 (2.26/sqrt(D)) dK 3.2e-2 and
+ * dQ 2.8e-2; 8 query heads per key/value head at D = 128 gave dV 2.07e-2 and
+ * 4 at head_dim 32 dK 2.01e-2 (dK and dV sum the rounding of every head of
+ * the group).
  *
  * Every token i of segment [s, e) attends to keys j with s <= j <= i and to
  * nothing else (one causal triangle per document, "Sample Packing：长序列 LLM
@@ -245,18 +261,46 @@ int psc_varlen_attn_fwd(int dtype, const void* q, const void* k, const void* v,
  *   out, lse: the forward's outputs for the same inputs.
  *   The workspace also carries -D_i (D_i = <dout_i, out_i>) and -lse_i / scale
  *   between the two kernels of the pass (dQ first, then dK/dV).
- *   dq [T, hq, D], dk [T, hkv, D], dv [T, hkv, D]: float32, contiguous
- *   (token stride heads*D).  dk and dv sum over the hq/hkv query heads of
- *   each key/value head.  All three are written in full.
+ *   grad_dtype: PSC_F32 (dq, dk, dv float32) or, for PSC_BF16 inputs only,
+ *   PSC_BF16 (each gradient accumulated in fp32 and rounded to bf16 once, to
+ *   nearest even, when stored; a bf16 gradient therefore also carries that
+ *   rounding, half a bf16 ulp of its value).  PSC_F32 inputs with PSC_BF16
+ *   gradients: PSC_ERR_UNSUPPORTED; any other grad_dtype: PSC_ERR_INVALID.
+ *   dq [T, hq, D], dk [T, hkv, D], dv [T, hkv, D] in grad_dtype, contiguous
+ *   (token stride heads*D), 16-byte aligned.  dk and dv sum over the hq/hkv
+ *   query heads of each key/value head.  All three are written in full.
  */
-int psc_varlen_attn_bwd(int dtype, const void* q, const void* k, const void* v,
+int psc_varlen_attn_bwd(int dtype, int grad_dtype, const void* q, const void* k, const void* v,
                         const void* out, const void* dout, const float* lse,
                         int64_t q_tok_stride, int64_t k_tok_stride, int64_t v_tok_stride,
                         int64_t out_tok_stride, int64_t dout_tok_stride,
                         const int32_t* cu_seqlens, int32_t n_segments, int32_t max_seqlen,
                         int64_t total_tokens, int32_t hq, int32_t hkv, int32_t head_dim,
-                        float softmax_scale, float* dq, float* dk, float* dv,
+                        float softmax_scale, void* dq, void* dk, void* dv,
                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * psc_check_cu_seqlens — device check of the cu_seqlens precondition
+ * (InternEvo "数据加载与流程", section "获取Dataloader数据": boundaries of the
+ * documents and padding of each row, from 0 to the packed length).  Enqueues
+ * one kernel on `stream` that reads cu_seqlens[0 .. n_segments] and writes
+ * flags[0] (int32, device) = 0 if 0 = c_0 < c_1 < ... < c_n = total_tokens,
+ * else the OR of PSC_CU_BAD_START (c_0 != 0), PSC_CU_BAD_END
+ * (c_n != total_tokens) and PSC_CU_NOT_INCREASING (some c_{i+1} <= c_i).
+ * Errors: PSC_ERR_INVALID (null pointer, negative or oversized sizes),
+ * PSC_ERR_HIP.
+ */
+enum { PSC_CU_BAD_START = 1, PSC_CU_BAD_END = 2, PSC_CU_NOT_INCREASING = 4 };
+int psc_check_cu_seqlens(const int32_t* cu_seqlens, int32_t n_segments, int64_t total_tokens,
+                         int32_t* flags, void* stream);
+
+/* psc_cu_seqlens_status — host-only: PSC_OK for a flags word of 0 from
+ * psc_check_cu_seqlens, PSC_ERR_INVALID for any other value. */
+int psc_cu_seqlens_status(int32_t flags);
+
+/* psc_debug_checks — 1 if this library was built with debug checks (the
+ * attention calls then validate cu_seqlens before launching), else 0. */
+int psc_debug_checks(void);
 
 /* ------------------------------------------------------------------------ */
 /* Instrumentation                                                           */

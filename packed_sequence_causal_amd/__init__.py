@@ -9,6 +9,7 @@ Entry points (same names as the C ABI without the ``psc_`` prefix):
   pack_sizes, pack_build                  build_pack / build_unpack on the GPU
   varlen_attn_workspace, varlen_attn_fwd, varlen_attn_bwd
                                           document-causal attention (bf16 or fp32)
+  check_cu_seqlens, cu_seqlens_status     device check of the cu_seqlens precondition
   rope                                    rotary embedding at the packer's indexes
   row_max_seqlen, unpack_data, split_sequence
                                           data steps after the packer
@@ -33,7 +34,8 @@ ERR_HIP = -5
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpsc.so")
-_lib = None
+DEBUG_LIB_PATH = os.path.join(_HERE, "libpsc_debug.so")
+_libs = {}
 
 _c_i64p = ctypes.POINTER(ctypes.c_int64)
 _c_sizep = ctypes.POINTER(ctypes.c_size_t)
@@ -58,11 +60,14 @@ _SIGNATURES = {
                                            ctypes.c_int64, _vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
                                            ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_float, _vp,
                                            ctypes.c_int64, _vp, _vp, ctypes.c_size_t, _vp]),
-    "psc_varlen_attn_bwd": (ctypes.c_int, [ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int64,
+    "psc_varlen_attn_bwd": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int64,
                                            ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, _vp,
                                            ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32,
                                            ctypes.c_int32, ctypes.c_int32, ctypes.c_float, _vp, _vp, _vp, _vp,
                                            ctypes.c_size_t, _vp]),
+    "psc_check_cu_seqlens": (ctypes.c_int, [_vp, ctypes.c_int32, ctypes.c_int64, _vp, _vp]),
+    "psc_cu_seqlens_status": (ctypes.c_int, [ctypes.c_int32]),
+    "psc_debug_checks": (ctypes.c_int, []),
     "psc_row_max_seqlen": (ctypes.c_int, [_vp, ctypes.c_int64, _vp, ctypes.c_int64, _vp, _vp]),
     "psc_unpack_data": (ctypes.c_int, [_vp, _vp, ctypes.c_int64, ctypes.c_int32, _vp, ctypes.c_int64, _vp, _vp,
                                        ctypes.c_int32, ctypes.c_int32, _vp, _vp, _vp]),
@@ -80,20 +85,25 @@ class PscError(RuntimeError):
         super().__init__(f"{where}: {strerror(status)} ({status})")
 
 
-def lib() -> ctypes.CDLL:
-    """Load libpsc.so (raises if it was not built)."""
-    global _lib
-    if _lib is None:
-        if not os.path.exists(LIB_PATH):
-            raise RuntimeError(f"{LIB_PATH} is missing; build it with __graft_entry__.build() "
-                               "or python -m packed_sequence_causal_amd.build")
-        L = ctypes.CDLL(LIB_PATH)
+def lib(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libpsc.so, or the library at `path` (raises if it was not built)."""
+    if path not in _libs:
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is missing; build it with __graft_entry__.build() "
+                               "or python -m packed_sequence_causal_amd.build --debug")
+        L = ctypes.CDLL(path)
         for name, (res, args) in _SIGNATURES.items():
             fn = getattr(L, name)
             fn.restype = res
             fn.argtypes = args
-        _lib = L
-    return _lib
+        _libs[path] = L
+    return _libs[path]
+
+
+def debug_lib() -> ctypes.CDLL:
+    """libpsc_debug.so: the same library built with device checks of
+    cu_seqlens before every attention launch."""
+    return lib(DEBUG_LIB_PATH)
 
 
 def strerror(status: int) -> str:
@@ -115,6 +125,25 @@ def _stream(stream):
     if stream is None:
         stream = torch.cuda.current_stream()
     return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _on(stream):
+    """Context in which the binding allocates: the caller's stream when one is
+    given, so torch's caching allocator never hands a block the kernels still
+    use on `stream` to work on another stream."""
+    import contextlib
+
+    import torch
+
+    return contextlib.nullcontext() if stream is None else torch.cuda.stream(stream)
+
+
+def _expect(t, name, shape, dtype, device):
+    """Raise ValueError unless t is a contiguous tensor of this shape and dtype
+    on `device` (the C ABI only sees a pointer and writes the full extent)."""
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype or t.device != device or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {dtype} tensor of shape {tuple(shape)} on {device}; got "
+                         f"{t.dtype} {tuple(t.shape)} on {t.device} (contiguous={t.is_contiguous()})")
 
 
 # ------------------------------------------------------------------ packing
@@ -145,19 +174,20 @@ def pack_build(tokens, doc_offsets, micro_bsz: int, seq_len: int, mode: int = PA
     rows, segs, ws = pack_sizes(mode, n_docs, n_tokens, micro_bsz, seq_len)
     dev = tokens.device
     PL = micro_bsz * seq_len
-    if out is None:
-        i32 = dict(dtype=torch.int32, device=dev)
-        out = {
-            "input_ids": torch.empty(rows, PL, **i32),
-            "labels": torch.empty(rows, PL, **i32),
-            "indexes": torch.empty(rows, PL, **i32),
-            "cu_seqlens": torch.empty(segs + 1, **i32),
-            "row_seg_ptr": torch.empty(rows + 1, **i32),
-            "row_valid_len": torch.empty(max(rows, 1), **i32),
-            "stats": torch.empty(4, **i32),
-        }
-    if workspace is None:
-        workspace = torch.empty(max(ws, 256), dtype=torch.uint8, device=dev)
+    with _on(stream):
+        if out is None:
+            i32 = dict(dtype=torch.int32, device=dev)
+            out = {
+                "input_ids": torch.empty(rows, PL, **i32),
+                "labels": torch.empty(rows, PL, **i32),
+                "indexes": torch.empty(rows, PL, **i32),
+                "cu_seqlens": torch.empty(segs + 1, **i32),
+                "row_seg_ptr": torch.empty(rows + 1, **i32),
+                "row_valid_len": torch.empty(max(rows, 1), **i32),
+                "stats": torch.empty(4, **i32),
+            }
+        if workspace is None:
+            workspace = torch.empty(max(ws, 256), dtype=torch.uint8, device=dev)
     _check(lib().psc_pack_build(mode, _ptr(tokens), _ptr(doc_offsets), n_docs, n_tokens, micro_bsz, seq_len,
                                 rows, _ptr(out["input_ids"]), _ptr(out["labels"]), _ptr(out["indexes"]),
                                 _ptr(out["cu_seqlens"]), out["cu_seqlens"].numel() - 1,
@@ -193,8 +223,24 @@ def varlen_attn_workspace(pass_: int, dtype: int, total_tokens: int, n_segments:
     return b.value
 
 
+def _check_inputs(q, k, v, cu_seqlens, nseg):
+    import torch
+
+    T, hq, D = q.shape
+    for name, t in (("k", k), ("v", v)):
+        if t.dim() != 3 or t.shape[0] != T or t.shape[2] != D or t.dtype != q.dtype or t.device != q.device:
+            raise ValueError(f"{name} must be [T, hkv, D] with q's T, D, dtype and device")
+    if v.shape[1] != k.shape[1]:
+        raise ValueError("k and v must have the same number of heads")
+    if cu_seqlens.dtype != torch.int32 or cu_seqlens.device != q.device or not cu_seqlens.is_contiguous():
+        raise ValueError("cu_seqlens must be a contiguous int32 tensor on q's device")
+    if cu_seqlens.numel() < nseg + 1:
+        raise ValueError("cu_seqlens must hold n_segments + 1 entries")
+
+
 def varlen_attn_fwd(q, k, v, cu_seqlens, max_seqlen: int, n_segments: Optional[int] = None,
-                    softmax_scale: Optional[float] = None, out=None, lse=None, workspace=None, stream=None):
+                    softmax_scale: Optional[float] = None, out=None, lse=None, workspace=None, stream=None,
+                    library=None):
     """Forward pass.  q [T,hq,D], k/v [T,hkv,D] (views allowed), cu_seqlens
     int32 [n_segments + 1].  Returns (out [T,hq,D], lse float32 [hq,T])."""
     import torch
@@ -203,14 +249,23 @@ def varlen_attn_fwd(q, k, v, cu_seqlens, max_seqlen: int, n_segments: Optional[i
     hkv = k.shape[1]
     dt = _dtype_code(q)
     nseg = cu_seqlens.numel() - 1 if n_segments is None else n_segments
-    if out is None:
-        out = torch.empty(T, hq, D, dtype=q.dtype, device=q.device)
-    if lse is None:
-        lse = torch.empty(hq, T, dtype=torch.float32, device=q.device)
-    ws = varlen_attn_workspace(0, dt, T, nseg, max_seqlen, hq, hkv, D)
-    if workspace is None or workspace.numel() < ws:
-        workspace = torch.empty(max(ws, 256), dtype=torch.uint8, device=q.device)
-    _check(lib().psc_varlen_attn_fwd(dt, _ptr(q), _ptr(k), _ptr(v), _tok_stride(q, "q"), _tok_stride(k, "k"),
+    _check_inputs(q, k, v, cu_seqlens, nseg)
+    L = library or lib()
+    b = ctypes.c_size_t()
+    _check(L.psc_varlen_attn_workspace(0, dt, T, nseg, max_seqlen, hq, hkv, D, ctypes.byref(b)),
+           "psc_varlen_attn_workspace")
+    ws = b.value
+    with _on(stream):
+        if out is None:
+            out = torch.empty(T, hq, D, dtype=q.dtype, device=q.device)
+        if lse is None:
+            lse = torch.empty(hq, T, dtype=torch.float32, device=q.device)
+        if workspace is None or workspace.numel() < ws:
+            workspace = torch.empty(max(ws, 256), dtype=torch.uint8, device=q.device)
+    if out.dim() != 3 or tuple(out.shape) != (T, hq, D) or out.dtype != q.dtype or out.device != q.device:
+        raise ValueError(f"out must be a {q.dtype} [T, hq, D] = {(T, hq, D)} tensor on {q.device}")
+    _expect(lse, "lse", (hq, T), torch.float32, q.device)
+    _check(L.psc_varlen_attn_fwd(dt, _ptr(q), _ptr(k), _ptr(v), _tok_stride(q, "q"), _tok_stride(k, "k"),
                                      _tok_stride(v, "v"), _ptr(cu_seqlens), nseg, max_seqlen, T, hq, hkv, D,
                                      float(softmax_scale or 0.0), _ptr(out), _tok_stride(out, "out"), _ptr(lse),
                                      _ptr(workspace), workspace.numel(), _stream(stream)), "psc_varlen_attn_fwd")
@@ -219,28 +274,70 @@ def varlen_attn_fwd(q, k, v, cu_seqlens, max_seqlen: int, n_segments: Optional[i
 
 def varlen_attn_bwd(q, k, v, out, dout, lse, cu_seqlens, max_seqlen: int, n_segments: Optional[int] = None,
                     softmax_scale: Optional[float] = None, dq=None, dk=None, dv=None, workspace=None,
-                    stream=None):
-    """Backward pass.  Returns fp32 (dq [T,hq,D], dk [T,hkv,D], dv [T,hkv,D])."""
+                    stream=None, grad_dtype: Optional[int] = None, library=None):
+    """Backward pass.  Returns (dq [T,hq,D], dk [T,hkv,D], dv [T,hkv,D]) in
+    float32, or bf16 with grad_dtype=BF16 (bf16 inputs only)."""
     import torch
 
     T, hq, D = q.shape
     hkv = k.shape[1]
     dt = _dtype_code(q)
+    gdt = F32 if grad_dtype is None else grad_dtype
     nseg = cu_seqlens.numel() - 1 if n_segments is None else n_segments
-    f32 = dict(dtype=torch.float32, device=q.device)
-    dq = torch.empty(T, hq, D, **f32) if dq is None else dq
-    dk = torch.empty(T, hkv, D, **f32) if dk is None else dk
-    dv = torch.empty(T, hkv, D, **f32) if dv is None else dv
-    ws = varlen_attn_workspace(1, dt, T, nseg, max_seqlen, hq, hkv, D)
-    if workspace is None or workspace.numel() < ws:
-        workspace = torch.empty(max(ws, 256), dtype=torch.uint8, device=q.device)
-    _check(lib().psc_varlen_attn_bwd(dt, _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse),
+    _check_inputs(q, k, v, cu_seqlens, nseg)
+    for name, t in (("out", out), ("dout", dout)):
+        if t.dim() != 3 or tuple(t.shape) != (T, hq, D) or t.dtype != q.dtype or t.device != q.device:
+            raise ValueError(f"{name} must be a {q.dtype} [T, hq, D] = {(T, hq, D)} tensor on {q.device}")
+    _expect(lse, "lse", (hq, T), torch.float32, q.device)
+    gtype = torch.bfloat16 if gdt == BF16 else torch.float32
+    L = library or lib()
+    b = ctypes.c_size_t()
+    _check(L.psc_varlen_attn_workspace(1, dt, T, nseg, max_seqlen, hq, hkv, D, ctypes.byref(b)),
+           "psc_varlen_attn_workspace")
+    ws = b.value
+    with _on(stream):
+        g = dict(dtype=gtype, device=q.device)
+        dq = torch.empty(T, hq, D, **g) if dq is None else dq
+        dk = torch.empty(T, hkv, D, **g) if dk is None else dk
+        dv = torch.empty(T, hkv, D, **g) if dv is None else dv
+        if workspace is None or workspace.numel() < ws:
+            workspace = torch.empty(max(ws, 256), dtype=torch.uint8, device=q.device)
+    _expect(dq, "dq", (T, hq, D), gtype, q.device)
+    _expect(dk, "dk", (T, hkv, D), gtype, q.device)
+    _expect(dv, "dv", (T, hkv, D), gtype, q.device)
+    _check(L.psc_varlen_attn_bwd(dt, gdt, _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse),
                                      _tok_stride(q, "q"), _tok_stride(k, "k"), _tok_stride(v, "v"),
                                      _tok_stride(out, "out"), _tok_stride(dout, "dout"), _ptr(cu_seqlens), nseg,
                                      max_seqlen, T, hq, hkv, D, float(softmax_scale or 0.0), _ptr(dq), _ptr(dk),
                                      _ptr(dv), _ptr(workspace), workspace.numel(), _stream(stream)),
            "psc_varlen_attn_bwd")
     return dq, dk, dv
+
+
+def check_cu_seqlens(cu_seqlens, total_tokens: int, n_segments: Optional[int] = None, flags=None, stream=None,
+                     library=None):
+    """Enqueue the device check of cu_seqlens (0 = c_0 < ... < c_n = T);
+    returns the int32 [1] flags tensor it writes (0 when the array is valid,
+    else the OR of CU_BAD_START, CU_BAD_END, CU_NOT_INCREASING)."""
+    import torch
+
+    nseg = cu_seqlens.numel() - 1 if n_segments is None else n_segments
+    if cu_seqlens.dtype != torch.int32 or not cu_seqlens.is_contiguous() or cu_seqlens.numel() < nseg + 1:
+        raise ValueError("cu_seqlens must be a contiguous int32 tensor with n_segments + 1 entries")
+    with _on(stream):
+        flags = torch.empty(1, dtype=torch.int32, device=cu_seqlens.device) if flags is None else flags
+    _expect(flags, "flags", (1,), torch.int32, cu_seqlens.device)
+    _check((library or lib()).psc_check_cu_seqlens(_ptr(cu_seqlens), nseg, total_tokens, _ptr(flags),
+                                                  _stream(stream)), "psc_check_cu_seqlens")
+    return flags
+
+
+CU_BAD_START, CU_BAD_END, CU_NOT_INCREASING = 1, 2, 4
+
+
+def cu_seqlens_status(flags: int) -> int:
+    """OK for a flags word of 0 from check_cu_seqlens, ERR_INVALID otherwise."""
+    return lib().psc_cu_seqlens_status(int(flags))
 
 
 # ---------------------------------------------------------- instrumentation

@@ -1,10 +1,14 @@
 """Build libpsc.so in-tree with hipcc for gfx950.
 
-    python -m packed_sequence_causal_amd.build        # or build() from Python
+    python -m packed_sequence_causal_amd.build          # release library
+    python -m packed_sequence_causal_amd.build --debug  # also libpsc_debug.so
 
 Every HIP source under csrc/ is compiled to an object in csrc/../_build and
-linked into packed_sequence_causal_amd/libpsc.so.  Packed-fp32 instruction
-selection is switched off for all device code.
+linked into packed_sequence_causal_amd/libpsc.so.  The debug variant
+(objects in _build_debug, library libpsc_debug.so) is the same code built with
+PSC_DEBUG_CHECKS: its attention calls validate cu_seqlens on the device before
+launching.  Packed-fp32 instruction selection is switched off for all device
+code.
 """
 from __future__ import annotations
 
@@ -18,6 +22,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libpsc.so")
+BUILD_DEBUG = os.path.join(PKG, "_build_debug")
+LIB_DEBUG = os.path.join(PKG, "libpsc_debug.so")
 ARCH = os.environ.get("PSC_OFFLOAD_ARCH", "gfx950")
 
 COMMON = [
@@ -43,34 +49,46 @@ def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
-def _compile(src):
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [_hipcc(), *COMMON, "-c", src, "-o", obj]
+def _compile(job):
+    src, outdir, extra = job
+    obj = os.path.join(outdir, os.path.basename(src) + ".o")
+    cmd = [_hipcc(), *COMMON, *extra, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stderr}")
     return obj, r.stderr
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    srcs = sources()
-    workers = max(1, min(len(srcs), int(os.environ.get("MAX_JOBS", os.cpu_count() or 4))))
+def _link(objs, lib):
+    tmp = lib + ".tmp"
+    cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stderr}")
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False, debug: bool = False) -> str:
+    """Compile and link libpsc.so (and libpsc_debug.so when debug=True)."""
+    variants = [(BUILD, LIB, [])]
+    if debug:
+        variants.append((BUILD_DEBUG, LIB_DEBUG, ["-DPSC_DEBUG_CHECKS"]))
+    jobs = []
+    for outdir, _, extra in variants:
+        os.makedirs(outdir, exist_ok=True)
+        jobs += [(src, outdir, extra) for src in sources()]
+    workers = max(1, min(len(jobs), int(os.environ.get("MAX_JOBS", os.cpu_count() or 4))))
     with ThreadPoolExecutor(workers) as ex:
-        results = list(ex.map(_compile, srcs))
+        results = list(ex.map(_compile, jobs))
     if verbose:
         for _, err in results:
             lines = [ln for ln in err.splitlines() if "packed-fp32-ops" not in ln and ln.strip()]
             if lines:
                 print("\n".join(lines), file=sys.stderr)
-    tmp = LIB + ".tmp"
-    cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *[o for o, _ in results]]
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    if r.returncode != 0:
-        raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB)
+    for outdir, lib, _ in variants:
+        _link([o for o, _ in results if os.path.dirname(o) == outdir], lib)
     return LIB
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    print(build(verbose="-v" in sys.argv, debug="--debug" in sys.argv))

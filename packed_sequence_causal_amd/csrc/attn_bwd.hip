@@ -47,7 +47,8 @@ struct BwdParams {
   const float* lse;
   float* Dbuf;   // [hq][T]  -D_i
   float* NLbuf;  // [hq][T]  -lse_i / scale
-  float *dq, *dk, *dv;
+  void *dq, *dk, *dv;  // float32, or bf16 when grad_bf16
+  int32_t grad_bf16;
   int64_t sq, sk, sv, so, sdo, T;
   const int32_t* cu;
   const int32_t* items;
@@ -156,8 +157,12 @@ __device__ __forceinline__ void dq_block(DqState<D>& st, const char* Ks, const c
 // 128 / HP rows: wave w takes head w % HP and rows 32 (w / HP) .. +31 of the
 // tile, so with HP = 4 all four waves cover the same rows (equal work) and
 // share every key/value block.
-template <int D, int HP>
+// DR = D / 2 runs heads of DR columns in the D-column kernel (as in the
+// forward): Q and dO are zero past DR in registers, so S, dP and D_i are those
+// of the head's columns, and only dQ's first DR columns are stored.
+template <int D, int HP, int DR = D>
 __global__ void __launch_bounds__(kThreads, 2) k_bwd_dq(BwdParams p) {
+  static_assert(DR == D || 2 * DR == D, "a head fills the tile or half of it");
   constexpr int RW = kBQ / HP;  // query rows per workgroup
   __shared__ __attribute__((aligned(16))) char Ks0[tile_bytes<D>()];
   __shared__ __attribute__((aligned(16))) char Vs0[tile_bytes<D>()];
@@ -172,36 +177,38 @@ __global__ void __launch_bounds__(kThreads, 2) k_bwd_dq(BwdParams p) {
   const int hw = w % HP, rs = w / HP;
   const int32_t head = (int32_t)hg * HP + hw;
   // item < cap (the grid is cap work-groups per head group), so the entry is read
-  // together with the count and used only once the count admits it.  Segment
-  // bounds come clamped to [0, T] from the schedule: a malformed cu_seqlens
-  // cannot send any access outside the tensors.
+  // together with the count and used only once the count admits it, and
+  // clamped to the token range (tile_item): a malformed cu_seqlens cannot
+  // send any access outside the tensors.
   const int4 it = *reinterpret_cast<const int4*>(p.items + 4 * item);
   if ((int32_t)item >= *p.n_items) return;
-  const int32_t s0 = it.x, L = it.y, tile = it.z;
+  TileItem ti;
+  if (!tile_item(it, p.T, RW, ti)) return;
+  const int32_t s0 = ti.s0, L = ti.L, tile = ti.tile;
   const int32_t q0 = tile * RW;
-  if (q0 >= L) return;
   const int32_t kvh = (int32_t)hg * HP / p.group;
 
-  const bf16* Kp = p.k + (int64_t)s0 * p.sk + (int64_t)kvh * D;
-  const bf16* Vp = p.v + (int64_t)s0 * p.sv + (int64_t)kvh * D;
+  const bf16* Kp = p.k + (int64_t)s0 * p.sk + (int64_t)kvh * DR;
+  const bf16* Vp = p.v + (int64_t)s0 * p.sv + (int64_t)kvh * DR;
   const int32_t kv_end = min(q0 + RW, L);
   const int32_t nkv = (kv_end + kBNq - 1) / kBNq;
   uint32_t koff[D / 8 / (kThreads / 64)], voff[D / 8 / (kThreads / 64)];
-  tile_offsets<D, kThreads / 64>(p.sk, w, l, koff);
-  tile_offsets<D, kThreads / 64>(p.sv, w, l, voff);
-  load_tile<D, kThreads / 64>(Kp, p.sk, 0, L, koff, Ks0, w, l);
-  load_tile<D, kThreads / 64>(Vp, p.sv, 0, L, voff, Vs0, w, l);
+  tile_offsets<D, kThreads / 64, DR>(p.sk, w, l, koff);
+  tile_offsets<D, kThreads / 64, DR>(p.sv, w, l, voff);
+  load_tile<D, kThreads / 64, DR>(Kp, p.sk, 0, L, koff, Ks0, w, l);
+  load_tile<D, kThreads / 64, DR>(Vp, p.sv, 0, L, voff, Vs0, w, l);
 
   const int32_t qrow = q0 + 32 * rs + lq;
   const bool qvalid = qrow < L;
   DqState<D> st;
   {
-    const bf16* Qr = p.q + (int64_t)(s0 + qrow) * p.sq + (int64_t)head * D;
-    const bf16* Dr = p.dout + (int64_t)(s0 + qrow) * p.sdo + (int64_t)head * D;
+    const bf16* Qr = p.q + (int64_t)(s0 + qrow) * p.sq + (int64_t)head * DR;
+    const bf16* Dr = p.dout + (int64_t)(s0 + qrow) * p.sdo + (int64_t)head * DR;
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) {
-      st.qf[kk] = qvalid ? *reinterpret_cast<const bf16x8*>(Qr + 16 * kk + 8 * h) : bf16x8{};
-      st.df[kk] = qvalid ? *reinterpret_cast<const bf16x8*>(Dr + 16 * kk + 8 * h) : bf16x8{};
+      const bool in = qvalid && 16 * kk + 8 * h < DR;
+      st.qf[kk] = in ? *reinterpret_cast<const bf16x8*>(Qr + 16 * kk + 8 * h) : bf16x8{};
+      st.df[kk] = in ? *reinterpret_cast<const bf16x8*>(Dr + 16 * kk + 8 * h) : bf16x8{};
     }
   }
   // D_i = <dO_i, O_i> from the dO fragments already held (lanes l and l ^ 32
@@ -211,9 +218,10 @@ __global__ void __launch_bounds__(kThreads, 2) k_bwd_dq(BwdParams p) {
   {
     float dacc = 0.f;
     if (qvalid) {
-      const bf16* Or = p.o + (int64_t)(s0 + qrow) * p.so + (int64_t)head * D;
+      const bf16* Or = p.o + (int64_t)(s0 + qrow) * p.so + (int64_t)head * DR;
 #pragma unroll
       for (int kk = 0; kk < D / 16; ++kk) {
+        if (16 * kk + 8 * h >= DR) continue;
         const bf16x8 of = *reinterpret_cast<const bf16x8*>(Or + 16 * kk + 8 * h);
 #pragma unroll
         for (int e = 0; e < 8; ++e) dacc = __builtin_fmaf((float)of[e], (float)st.df[kk][e], dacc);
@@ -237,16 +245,16 @@ __global__ void __launch_bounds__(kThreads, 2) k_bwd_dq(BwdParams p) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (j + 1 < nkv) {
-      load_tile<D, kThreads / 64>(Kp, p.sk, (j + 1) * kBNq, L, koff, Ks1, w, l);
-      load_tile<D, kThreads / 64>(Vp, p.sv, (j + 1) * kBNq, L, voff, Vs1, w, l);
+      load_tile<D, kThreads / 64, DR>(Kp, p.sk, (j + 1) * kBNq, L, koff, Ks1, w, l);
+      load_tile<D, kThreads / 64, DR>(Vp, p.sv, (j + 1) * kBNq, L, voff, Vs1, w, l);
     }
     if (j * kBNq <= wq_top) dq_block<D>(st, Ks0, Vs0, j * kBNq, L, qrow, wq_lo, c2, h, lq, l);
     if (j + 1 >= nkv) break;
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (j + 2 < nkv) {
-      load_tile<D, kThreads / 64>(Kp, p.sk, (j + 2) * kBNq, L, koff, Ks0, w, l);
-      load_tile<D, kThreads / 64>(Vp, p.sv, (j + 2) * kBNq, L, voff, Vs0, w, l);
+      load_tile<D, kThreads / 64, DR>(Kp, p.sk, (j + 2) * kBNq, L, koff, Ks0, w, l);
+      load_tile<D, kThreads / 64, DR>(Vp, p.sv, (j + 2) * kBNq, L, voff, Vs0, w, l);
     }
     if ((j + 1) * kBNq <= wq_top) dq_block<D>(st, Ks1, Vs1, (j + 1) * kBNq, L, qrow, wq_lo, c2, h, lq, l);
   }
@@ -257,13 +265,39 @@ __global__ void __launch_bounds__(kThreads, 2) k_bwd_dq(BwdParams p) {
   // consumed before the last barrier, and no load targets it); each wave
   // stages its 32 rows in its own half of one of its tiles, kPW columns at a
   // time.  Inside a staged row, 16-byte chunk c sits at slot c ^ (row % kPC).
-  {
+  char* const stage = (nkv & 1) ? (w < 2 ? Ks1 : Vs1) : (w < 2 ? Ks0 : Vs0);
+  char* const ob = stage + (w & 1) * (tile_bytes<D>() / 2);
+  if (p.grad_bf16) {
+    // bf16 dQ: whole 2*D-byte rows fit half a tile at once (as the forward's O)
+    constexpr int kChunks = D / 8;
+    bf16* const dq = static_cast<bf16*>(p.dq);
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) {
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        bf16x4 o4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o4[e] = (bf16)(st.acc[dt][4 * g4 + e] * p.scale);
+        const int c = 4 * dt + g4;
+        *reinterpret_cast<bf16x4*>(ob + lq * (2 * D) + ((c ^ (lq & (kChunks - 1))) << 4) + 8 * h) = o4;
+      }
+    }
+    constexpr int kRowsPerStore = 64 / kChunks;
+    const int c = l % kChunks;
+#pragma unroll
+    for (int k = 0; k < 32 / kRowsPerStore; ++k) {
+      const int r = k * kRowsPerStore + l / kChunks;
+      const bf16x8 v8 = *reinterpret_cast<const bf16x8*>(ob + r * (2 * D) + ((c ^ (r & (kChunks - 1))) << 4));
+      const int32_t row = wq_lo + r;
+      if (row < L && 8 * c < DR) *reinterpret_cast<bf16x8*>(dq + ((int64_t)(s0 + row) * p.hq + head) * DR + 8 * c) = v8;
+    }
+  } else {
     constexpr int kPW = tile_bytes<D>() / 256;  // fp32 columns per pass: 32 rows x kPW x 4 B = half a tile
     constexpr int kPC = kPW / 4;                 // 16-byte chunks per staged row
-    char* stage = (nkv & 1) ? (w < 2 ? Ks1 : Vs1) : (w < 2 ? Ks0 : Vs0);
-    char* ob = stage + (w & 1) * (tile_bytes<D>() / 2);
+    static_assert(DR % kPW == 0, "passes cover whole heads");
+    float* const dq = static_cast<float*>(p.dq);
 #pragma unroll
-    for (int pass = 0; pass < D / kPW; ++pass) {
+    for (int pass = 0; pass < DR / kPW; ++pass) {
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) {
         if ((32 * dt) / kPW != pass) continue;
@@ -283,7 +317,7 @@ __global__ void __launch_bounds__(kThreads, 2) k_bwd_dq(BwdParams p) {
         const int r = k * kRowsPerStore + l / kPC;
         const f32x4 v4 = *reinterpret_cast<const f32x4*>(ob + r * (4 * kPW) + ((c ^ (r & (kPC - 1))) << 4));
         const int32_t row = wq_lo + r;
-        if (row < L) *reinterpret_cast<f32x4*>(p.dq + ((int64_t)(s0 + row) * p.hq + head) * D + kPW * pass + 4 * c) = v4;
+        if (row < L) *reinterpret_cast<f32x4*>(dq + ((int64_t)(s0 + row) * p.hq + head) * DR + kPW * pass + 4 * c) = v4;
       }
     }
   }
@@ -502,9 +536,13 @@ __device__ __forceinline__ void dkdv_block_full(DkvState<D>& st, const char* Qs,
 // D = 64 only (two waves per SIMD).  At D = 128 the K, V operands and dK, dV
 // accumulators of 32 keys need ~360 registers, one wave per SIMD, and the
 // eight-wave kernel below runs instead.
-template <int D>
+// DR = D / 2 runs heads of DR columns: K and V are zero past DR in registers
+// (S and dP are those of the head's columns), and only the first DR columns of
+// dK and dV are stored.
+template <int D, int DR = D>
 __global__ void __launch_bounds__(kThreads, 2) k_bwd_dkdv(BwdParams p) {
   static_assert(D == 64, "k_bwd_dkdv8 handles D = 128");
+  static_assert(DR == D || 2 * DR == D, "a head fills the tile or half of it");
   __shared__ __attribute__((aligned(16))) char Qs0[tile_bytes<D>()];
   __shared__ __attribute__((aligned(16))) char dOs0[tile_bytes<D>()];
   __shared__ __attribute__((aligned(16))) char Qs1[tile_bytes<D>()];
@@ -517,14 +555,15 @@ __global__ void __launch_bounds__(kThreads, 2) k_bwd_dkdv(BwdParams p) {
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, h = l >> 5, lq = l & 31;
   const uint32_t item = blockIdx.x / (uint32_t)p.hkv, kvh = blockIdx.x % (uint32_t)p.hkv;
   // item < cap (the grid is cap work-groups per head), so the entry is read
-  // together with the count and used only once the count admits it.  Segment
-  // bounds come clamped to [0, T] from the schedule: a malformed cu_seqlens
-  // cannot send any access outside the tensors.
+  // together with the count and used only once the count admits it, and
+  // clamped to the token range (tile_item): a malformed cu_seqlens cannot
+  // send any access outside the tensors.
   const int4 it = *reinterpret_cast<const int4*>(p.items + 4 * item);
   if ((int32_t)item >= *p.n_items) return;
-  const int32_t s0 = it.x, L = it.y, tile = it.z;
+  TileItem ti;
+  if (!tile_item(it, p.T, kBKV, ti)) return;
+  const int32_t s0 = ti.s0, L = ti.L, tile = ti.tile;
   const int32_t kb = tile * kBKV;
-  if (kb >= L) return;
   const int32_t key = kb + 32 * w + lq;  // this lane's key (S layout: lane <-> key)
   const bool kvalid = key < L;
   const int32_t wk_lo = kb + 32 * w;
@@ -532,8 +571,8 @@ __global__ void __launch_bounds__(kThreads, 2) k_bwd_dkdv(BwdParams p) {
   const int32_t niter = p.group * nqb;
 
   uint32_t qoff[D / 8 / (kThreads / 64)], ooff[D / 8 / (kThreads / 64)];
-  tile_offsets<D, kThreads / 64>(p.sq, w, l, qoff);
-  tile_offsets<D, kThreads / 64>(p.sdo, w, l, ooff);
+  tile_offsets<D, kThreads / 64, DR>(p.sq, w, l, qoff);
+  tile_offsets<D, kThreads / 64, DR>(p.sdo, w, l, ooff);
   // iteration t: query head kvh*G + t / nqb, query block kb + (nqb - 1 - t % nqb) * 64.
   // Blocks run from the document end back to the tile: every tile of a
   // document starts at the same rows, so tiles of one document that run at
@@ -541,8 +580,8 @@ __global__ void __launch_bounds__(kThreads, 2) k_bwd_dkdv(BwdParams p) {
   auto issue = [&](int32_t t, char* Qs, char* dOs, float* NLs, float* Ds) {
     const int32_t head = kvh * p.group + t / nqb;
     const int32_t qs = kb + (nqb - 1 - t % nqb) * kBMk;
-    load_tile<D, kThreads / 64>(p.q + (int64_t)s0 * p.sq + (int64_t)head * D, p.sq, qs, L, qoff, Qs, w, l);
-    load_tile<D, kThreads / 64>(p.dout + (int64_t)s0 * p.sdo + (int64_t)head * D, p.sdo, qs, L, ooff, dOs, w, l);
+    load_tile<D, kThreads / 64, DR>(p.q + (int64_t)s0 * p.sq + (int64_t)head * DR, p.sq, qs, L, qoff, Qs, w, l);
+    load_tile<D, kThreads / 64, DR>(p.dout + (int64_t)s0 * p.sdo + (int64_t)head * DR, p.sdo, qs, L, ooff, dOs, w, l);
     if (w == 0) load_vec64_async(p.NLbuf + (int64_t)head * p.T + s0, qs, L, NLs, l);
     if (w == 1) load_vec64_async(p.Dbuf + (int64_t)head * p.T + s0, qs, L, Ds, l);
   };
@@ -550,12 +589,13 @@ __global__ void __launch_bounds__(kThreads, 2) k_bwd_dkdv(BwdParams p) {
 
   DkvState<D> st;
   {
-    const bf16* Kr = p.k + (int64_t)(s0 + key) * p.sk + (int64_t)kvh * D;
-    const bf16* Vr = p.v + (int64_t)(s0 + key) * p.sv + (int64_t)kvh * D;
+    const bf16* Kr = p.k + (int64_t)(s0 + key) * p.sk + (int64_t)kvh * DR;
+    const bf16* Vr = p.v + (int64_t)(s0 + key) * p.sv + (int64_t)kvh * DR;
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) {
-      st.kf[kk] = kvalid ? *reinterpret_cast<const bf16x8*>(Kr + 16 * kk + 8 * h) : bf16x8{};
-      st.vf[kk] = kvalid ? *reinterpret_cast<const bf16x8*>(Vr + 16 * kk + 8 * h) : bf16x8{};
+      const bool in = kvalid && 16 * kk + 8 * h < DR;
+      st.kf[kk] = in ? *reinterpret_cast<const bf16x8*>(Kr + 16 * kk + 8 * h) : bf16x8{};
+      st.vf[kk] = in ? *reinterpret_cast<const bf16x8*>(Vr + 16 * kk + 8 * h) : bf16x8{};
     }
   }
 #pragma unroll
@@ -595,12 +635,16 @@ __global__ void __launch_bounds__(kThreads, 2) k_bwd_dkdv(BwdParams p) {
   for (int i = 0; i < 16; ++i) {
     const int32_t kr = wk_lo + 8 * (i >> 2) + 4 * h + (i & 3);
     if (kr < L) {
-      float* dkr = p.dk + ((int64_t)(s0 + kr) * p.hkv + kvh) * D;
-      float* dvr = p.dv + ((int64_t)(s0 + kr) * p.hkv + kvh) * D;
+      const int64_t row = ((int64_t)(s0 + kr) * p.hkv + kvh) * DR;
 #pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt) {
-        dkr[32 * dt + lq] = st.dka[dt][i] * p.scale;
-        dvr[32 * dt + lq] = st.dva[dt][i];
+      for (int dt = 0; dt < DR / 32; ++dt) {
+        if (p.grad_bf16) {
+          static_cast<bf16*>(p.dk)[row + 32 * dt + lq] = (bf16)(st.dka[dt][i] * p.scale);
+          static_cast<bf16*>(p.dv)[row + 32 * dt + lq] = (bf16)st.dva[dt][i];
+        } else {
+          static_cast<float*>(p.dk)[row + 32 * dt + lq] = st.dka[dt][i] * p.scale;
+          static_cast<float*>(p.dv)[row + 32 * dt + lq] = st.dva[dt][i];
+        }
       }
     }
   }
@@ -742,13 +786,14 @@ __global__ void __launch_bounds__(kThreads8, 1) k_bwd_dkdv8(BwdParams p) {
   const int ks = w & 3, qh = w >> 2;
   const uint32_t item = blockIdx.x / (uint32_t)p.hkv, kvh = blockIdx.x % (uint32_t)p.hkv;
   // item < cap (the grid is cap work-groups per head), so the entry is read
-  // together with the count and used only once the count admits it.  Segment
-  // bounds come clamped to [0, T] from the schedule.
+  // together with the count and used only once the count admits it, and
+  // clamped to the token range (tile_item).
   const int4 it = *reinterpret_cast<const int4*>(p.items + 4 * item);
   if ((int32_t)item >= *p.n_items) return;
-  const int32_t s0 = it.x, L = it.y, tile = it.z;
+  TileItem ti;
+  if (!tile_item(it, p.T, kBKV, ti)) return;
+  const int32_t s0 = ti.s0, L = ti.L, tile = ti.tile;
   const int32_t kb = tile * kBKV;
-  if (kb >= L) return;
   const int32_t wk_lo = kb + 32 * ks;
   const int32_t key = wk_lo + lq;  // this lane's key (S layout: lane <-> key)
   const int32_t nqb = (L - kb + kBMk - 1) / kBMk;
@@ -828,7 +873,7 @@ __global__ void __launch_bounds__(kThreads8, 1) k_bwd_dkdv8(BwdParams p) {
     }
   };
   // add the partner's part and store (C layout: key = wk_lo + 8*(i/4) + 4*h + i%4, d = 32*dt + lq)
-  auto finish = [&](f32x16* x, float* outp, float mul) {
+  auto finish = [&](f32x16* x, void* outp, float mul) {
     const f32x4* theirs = red + (2 * ks + (qh ^ 1)) * kPieces;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
@@ -843,9 +888,14 @@ __global__ void __launch_bounds__(kThreads8, 1) k_bwd_dkdv8(BwdParams p) {
     for (int i = 0; i < 16; ++i) {
       const int32_t kr = wk_lo + 8 * (i >> 2) + 4 * h + (i & 3);
       if (kr < L) {
-        float* r = outp + ((int64_t)(s0 + kr) * p.hkv + kvh) * D;
+        const int64_t row = ((int64_t)(s0 + kr) * p.hkv + kvh) * D;
+        if (p.grad_bf16) {
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) r[32 * dt + lq] = x[dt][i] * mul;
+          for (int dt = 0; dt < DT; ++dt) static_cast<bf16*>(outp)[row + 32 * dt + lq] = (bf16)(x[dt][i] * mul);
+        } else {
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) static_cast<float*>(outp)[row + 32 * dt + lq] = x[dt][i] * mul;
+        }
       }
     }
   };
@@ -897,6 +947,7 @@ hipError_t launch_attn_bwd_bf16(const AttnBwdArgs& a, hipStream_t stream) {
   p.dq = a.dq;
   p.dk = a.dk;
   p.dv = a.dv;
+  p.grad_bf16 = a.grad_bf16;
   p.sq = a.sq;
   p.sk = a.sk;
   p.sv = a.sv;
@@ -923,10 +974,15 @@ hipError_t launch_attn_bwd_bf16(const AttnBwdArgs& a, hipStream_t stream) {
       if (hp == 4) k_bwd_dq<128, 4><<<grid_q, kThreads, 0, stream>>>(p);
       else if (hp == 2) k_bwd_dq<128, 2><<<grid_q, kThreads, 0, stream>>>(p);
       else k_bwd_dq<128, 1><<<grid_q, kThreads, 0, stream>>>(p);
-    } else {
+    } else if (d.d == 64) {
       if (hp == 4) k_bwd_dq<64, 4><<<grid_q, kThreads, 0, stream>>>(p);
       else if (hp == 2) k_bwd_dq<64, 2><<<grid_q, kThreads, 0, stream>>>(p);
       else k_bwd_dq<64, 1><<<grid_q, kThreads, 0, stream>>>(p);
+    } else {
+      // head_dim 32: the D = 64 kernel on half-width heads
+      if (hp == 4) k_bwd_dq<64, 4, 32><<<grid_q, kThreads, 0, stream>>>(p);
+      else if (hp == 2) k_bwd_dq<64, 2, 32><<<grid_q, kThreads, 0, stream>>>(p);
+      else k_bwd_dq<64, 1, 32><<<grid_q, kThreads, 0, stream>>>(p);
     }
   }
 
@@ -939,8 +995,10 @@ hipError_t launch_attn_bwd_bf16(const AttnBwdArgs& a, hipStream_t stream) {
     ScopedKernelTimer timed(kTimeBwdDkdv, stream);
     if (d.d == 128)
       k_bwd_dkdv8<128><<<grid_kv, kThreads8, 0, stream>>>(p);
-    else
+    else if (d.d == 64)
       k_bwd_dkdv<64><<<grid_kv, kThreads, 0, stream>>>(p);
+    else
+      k_bwd_dkdv<64, 32><<<grid_kv, kThreads, 0, stream>>>(p);
   }
   return hipGetLastError();
 }

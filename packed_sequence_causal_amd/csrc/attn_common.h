@@ -146,7 +146,11 @@ __device__ __forceinline__ int lds_byte(int r, int e) {
 // swizzle places at its slot.  Rows at or past `L` repeat row L - 1: their
 // scores are masked, any finite data will do.  Completion is tracked by
 // vmcnt; wait, then barrier, before reading the tile.
-template <int D, int NW>
+// DR < D (a head of DR = D/2 columns held in a D-column tile): chunk c of a
+// row is fetched from chunk c mod DR/8, so the columns past the head repeat
+// its first ones; the kernels zero those columns of their register operand
+// (scores are unchanged) or drop the results that read them.
+template <int D, int NW, int DR = D>
 __device__ __forceinline__ void load_tile_async(const bf16* base, int64_t stride, int32_t row0, int32_t L,
                                                 void* lds, int w, int l) {
   constexpr int LOADS = D / 8;  // 64 rows x D/8 chunks / 64 lanes
@@ -161,7 +165,7 @@ __device__ __forceinline__ void load_tile_async(const bf16* base, int64_t stride
     const int tu = wu + NW * i;
     const int g = t >> 3;
     const int r = 8 * (t & 7) + rr;
-    const int c = 8 * g + (p ^ lds_swz(r));
+    const int c = (8 * g + (p ^ lds_swz(r))) % (DR / 8);
     const bf16* src = base + (int64_t)min(row0 + r, L - 1) * stride + c * 8;
     lds_dma16(src, lds0 + (tu >> 3) * kGroupBytes + (tu & 7) * 1024);
   }
@@ -170,7 +174,7 @@ __device__ __forceinline__ void load_tile_async(const bf16* base, int64_t stride
 // Per-lane byte offsets (from the tile's first row) of the chunks this wave
 // fetches in load_tile_async, for a tile that needs no row clamping.
 // stride * 128 must stay below 2^32 (checked by the host API).
-template <int D, int NW>
+template <int D, int NW, int DR = D>
 __device__ __forceinline__ void tile_offsets(int64_t stride, int w, int l, uint32_t* off) {
   constexpr int LOADS = D / 8;
   const int rr = l >> 3;
@@ -180,7 +184,7 @@ __device__ __forceinline__ void tile_offsets(int64_t stride, int w, int l, uint3
     const int t = w + NW * i;
     const int g = t >> 3;
     const int r = 8 * (t & 7) + rr;
-    const int c = 8 * g + (p ^ lds_swz(r));
+    const int c = (8 * g + (p ^ lds_swz(r))) % (DR / 8);
     off[i] = (uint32_t)(((int64_t)r * stride + c * 8) * 2);
   }
 }
@@ -200,14 +204,14 @@ __device__ __forceinline__ void load_tile_async_full(const bf16* rows, const uin
 }
 
 // load_tile_async with the offset-only fast path for tiles inside the
-// segment (`off` from tile_offsets for this stride).
-template <int D, int NW>
+// segment (`off` from tile_offsets<D, NW, DR> for this stride).
+template <int D, int NW, int DR = D>
 __device__ __forceinline__ void load_tile(const bf16* base, int64_t stride, int32_t row0, int32_t L,
                                           const uint32_t* off, void* lds, int w, int l) {
   if (row0 + kTileRows <= L)
     load_tile_async_full<D, NW>(base + (int64_t)row0 * stride, off, lds, w);
   else
-    load_tile_async<D, NW>(base, stride, row0, L, lds, w, l);
+    load_tile_async<D, NW, DR>(base, stride, row0, L, lds, w, l);
 }
 
 // Asynchronous load of 64 consecutive floats vec[row0 .. row0 + 64) (rows at or
@@ -215,6 +219,22 @@ __device__ __forceinline__ void load_tile(const bf16* base, int64_t stride, int3
 __device__ __forceinline__ void load_vec64_async(const float* vec, int32_t row0, int32_t L, void* lds, int l) {
   const int32_t row = min(row0 + l, L - 1);
   lds_dma4(vec + row, lds_addr(lds));
+}
+
+// A schedule entry (segment start, segment length, tile index) clamped to the
+// token range [0, T).  The list is built on the device from cu_seqlens, and a
+// cu_seqlens that breaks its precondition can leave slots unwritten; clamped,
+// no entry can address outside the tensors.  Returns false when the tile lies
+// past its segment (nothing to do).
+struct TileItem {
+  int32_t s0, L, tile;
+};
+__device__ __forceinline__ bool tile_item(const int4& it, int64_t T, int rows, TileItem& out) {
+  const int32_t t = (int32_t)T;
+  out.s0 = min(max(it.x, 0), t);
+  out.L = min(max(it.y, 0), t - out.s0);
+  out.tile = it.z;
+  return it.z >= 0 && out.L > 0 && it.z <= (out.L - 1) / rows;
 }
 
 // Scheduling hints: keep `n` LDS reads / MFMAs / VALU ops together, in the

@@ -212,9 +212,9 @@ hipError_t launch_attn_bwd_f32(const AttnBwdArgs& a, hipStream_t stream) {
   p.dout = static_cast<const float*>(a.dout);
   p.lse_in = a.lse;
   p.Dbuf = static_cast<float*>(a.workspace);
-  p.dq = a.dq;
-  p.dk = a.dk;
-  p.dv = a.dv;
+  p.dq = static_cast<float*>(a.dq);
+  p.dk = static_cast<float*>(a.dk);
+  p.dv = static_cast<float*>(a.dv);
   p.sq = a.sq;
   p.sk = a.sk;
   p.sv = a.sv;

@@ -51,12 +51,12 @@ struct FwdParams {
 };
 
 // Asynchronous loads of key/value rows [kb, kb + 64) into one LDS stage.
-template <int D>
+template <int D, int DR>
 __device__ __forceinline__ void load_kv(const bf16* Kp, const bf16* Vp, int64_t sk, int64_t sv, int32_t kb,
                                         int32_t L, char* Ks, char* Vs, const uint32_t* koff, const uint32_t* voff,
                                         int w, int l) {
-  load_tile<D, kThreads / 64>(Kp, sk, kb, L, koff, Ks, w, l);
-  load_tile<D, kThreads / 64>(Vp, sv, kb, L, voff, Vs, w, l);
+  load_tile<D, kThreads / 64, DR>(Kp, sk, kb, L, koff, Ks, w, l);
+  load_tile<D, kThreads / 64, DR>(Vp, sv, kb, L, voff, Vs, w, l);
 }
 
 template <int D>
@@ -126,8 +126,13 @@ __device__ __forceinline__ void fwd_block(FwdState<D>& st, const char* Ks, const
 // 128 / HP rows: wave w takes head w % HP and rows 32 (w / HP) .. +31 of the
 // tile, so with HP = 4 all four waves cover the same rows (equal work) and
 // share every key/value block.
-template <int D, int HP>
+// DR = D / 2 runs heads of DR columns in the D-column kernel: Q's columns past
+// DR are zero in registers (so the scores are those of the DR columns), the
+// tile loader repeats the head's columns there, and only O's first DR
+// columns are stored.
+template <int D, int HP, int DR = D>
 __global__ void __launch_bounds__(kThreads, 2) k_attn_fwd(FwdParams p) {
+  static_assert(DR == D || 2 * DR == D, "a head fills the tile or half of it");
   constexpr int RW = kBM / HP;  // query rows per workgroup
   __shared__ __attribute__((aligned(16))) char Ks0[tile_bytes<D>()];
   __shared__ __attribute__((aligned(16))) char Vs0[tile_bytes<D>()];
@@ -142,34 +147,36 @@ __global__ void __launch_bounds__(kThreads, 2) k_attn_fwd(FwdParams p) {
   const int hw = w % HP, rs = w / HP;
   const int32_t head = (int32_t)hg * HP + hw;
   // item < cap (the grid is cap work-groups per head), so the entry is read
-  // together with the count and used only once the count admits it.  Segment
-  // bounds come clamped to [0, T] from the schedule: a malformed cu_seqlens
-  // cannot send any access outside the tensors.
+  // together with the count and used only once the count admits it, and
+  // clamped to the token range (tile_item): a malformed cu_seqlens cannot
+  // send any access outside the tensors.
   const int4 it = *reinterpret_cast<const int4*>(p.items + 4 * item);
   if ((int32_t)item >= *p.n_items) return;
-  const int32_t s0 = it.x, L = it.y, tile = it.z;
+  TileItem ti;
+  if (!tile_item(it, p.T, RW, ti)) return;
+  const int32_t s0 = ti.s0, L = ti.L, tile = ti.tile;
   const int32_t q0 = tile * RW;
-  if (q0 >= L) return;
   const int32_t kvh = (int32_t)hg * HP / p.group;
 
-  const bf16* Qp = p.q + (int64_t)s0 * p.sq + (int64_t)head * D;
-  const bf16* Kp = p.k + (int64_t)s0 * p.sk + (int64_t)kvh * D;
-  const bf16* Vp = p.v + (int64_t)s0 * p.sv + (int64_t)kvh * D;
+  const bf16* Qp = p.q + (int64_t)s0 * p.sq + (int64_t)head * DR;
+  const bf16* Kp = p.k + (int64_t)s0 * p.sk + (int64_t)kvh * DR;
+  const bf16* Vp = p.v + (int64_t)s0 * p.sv + (int64_t)kvh * DR;
 
   const int32_t kv_end = min(q0 + RW, L);
   const int32_t nkv = (kv_end + kBN - 1) / kBN;
   uint32_t koff[D / 8 / (kThreads / 64)], voff[D / 8 / (kThreads / 64)];
-  tile_offsets<D, kThreads / 64>(p.sk, w, l, koff);
-  tile_offsets<D, kThreads / 64>(p.sv, w, l, voff);
-  load_kv<D>(Kp, Vp, p.sk, p.sv, 0, L, Ks0, Vs0, koff, voff, w, l);
+  tile_offsets<D, kThreads / 64, DR>(p.sk, w, l, koff);
+  tile_offsets<D, kThreads / 64, DR>(p.sv, w, l, voff);
+  load_kv<D, DR>(Kp, Vp, p.sk, p.sv, 0, L, Ks0, Vs0, koff, voff, w, l);
 
   const int32_t qrow = q0 + 32 * rs + lq;
   const bool qvalid = qrow < L;
   FwdState<D> st;
 #pragma unroll
   for (int kk = 0; kk < D / 16; ++kk) {
-    st.qf[kk] = qvalid ? *reinterpret_cast<const bf16x8*>(Qp + (int64_t)qrow * p.sq + 16 * kk + 8 * h)
-                       : bf16x8{};
+    st.qf[kk] = qvalid && 16 * kk + 8 * h < DR
+                    ? *reinterpret_cast<const bf16x8*>(Qp + (int64_t)qrow * p.sq + 16 * kk + 8 * h)
+                    : bf16x8{};
   }
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) st.oacc[dt] = f32x16{};
@@ -186,13 +193,13 @@ __global__ void __launch_bounds__(kThreads, 2) k_attn_fwd(FwdParams p) {
     // stage 0 holds block j
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (j + 1 < nkv) load_kv<D>(Kp, Vp, p.sk, p.sv, (j + 1) * kBN, L, Ks1, Vs1, koff, voff, w, l);
+    if (j + 1 < nkv) load_kv<D, DR>(Kp, Vp, p.sk, p.sv, (j + 1) * kBN, L, Ks1, Vs1, koff, voff, w, l);
     if (j * kBN <= wq_top) fwd_block<D>(st, Ks0, Vs0, j * kBN, L, qrow, wq_lo, c2, h, ro);
     if (j + 1 >= nkv) break;
     // stage 1 holds block j + 1
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (j + 2 < nkv) load_kv<D>(Kp, Vp, p.sk, p.sv, (j + 2) * kBN, L, Ks0, Vs0, koff, voff, w, l);
+    if (j + 2 < nkv) load_kv<D, DR>(Kp, Vp, p.sk, p.sv, (j + 2) * kBN, L, Ks0, Vs0, koff, voff, w, l);
     if ((j + 1) * kBN <= wq_top) fwd_block<D>(st, Ks1, Vs1, (j + 1) * kBN, L, qrow, wq_lo, c2, h, ro);
   }
 
@@ -226,7 +233,8 @@ __global__ void __launch_bounds__(kThreads, 2) k_attn_fwd(FwdParams p) {
       const int r = k * kRowsPerStore + l / kChunks;
       const bf16x8 v8 = *reinterpret_cast<const bf16x8*>(ob + r * (2 * D) + ((c ^ (r & (kChunks - 1))) << 4));
       const int32_t row = wq_lo + r;
-      if (row < L) *reinterpret_cast<bf16x8*>(p.out + (int64_t)(s0 + row) * p.so + (int64_t)head * D + 8 * c) = v8;
+      if (row < L && 8 * c < DR)
+        *reinterpret_cast<bf16x8*>(p.out + (int64_t)(s0 + row) * p.so + (int64_t)head * DR + 8 * c) = v8;
     }
   }
   if (qvalid && h == 0) p.lse[(int64_t)head * p.T + s0 + qrow] = (st.m_i + __log2f(lt)) * kLn2;
@@ -276,10 +284,15 @@ hipError_t launch_attn_fwd_bf16(const AttnFwdArgs& a, hipStream_t stream) {
     if (hp == 4) k_attn_fwd<128, 4><<<g, kThreads, 0, stream>>>(p);
     else if (hp == 2) k_attn_fwd<128, 2><<<g, kThreads, 0, stream>>>(p);
     else k_attn_fwd<128, 1><<<g, kThreads, 0, stream>>>(p);
-  } else {
+  } else if (d.d == 64) {
     if (hp == 4) k_attn_fwd<64, 4><<<g, kThreads, 0, stream>>>(p);
     else if (hp == 2) k_attn_fwd<64, 2><<<g, kThreads, 0, stream>>>(p);
     else k_attn_fwd<64, 1><<<g, kThreads, 0, stream>>>(p);
+  } else {
+    // head_dim 32: the D = 64 kernel on half-width heads
+    if (hp == 4) k_attn_fwd<64, 4, 32><<<g, kThreads, 0, stream>>>(p);
+    else if (hp == 2) k_attn_fwd<64, 2, 32><<<g, kThreads, 0, stream>>>(p);
+    else k_attn_fwd<64, 1, 32><<<g, kThreads, 0, stream>>>(p);
   }
   return hipGetLastError();
 }

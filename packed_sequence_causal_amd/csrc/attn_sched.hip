@@ -33,10 +33,13 @@ __device__ inline int32_t seg_len(const int32_t* cu, int32_t s, int32_t T) {
 }
 
 // One block: zero the histogram, count each segment's tiles and scan them
-// into toff[0..n_seg] (toff[n_seg] = number of tiles, also stored in n_items).
+// into toff[0..n_seg] (toff[n_seg] = number of tiles).  n_items gets that
+// count clamped to the list's capacity: only a cu_seqlens that breaks its
+// precondition can exceed it, and consumers must never read past the entries
+// k_sched_fill wrote.
 __global__ void __launch_bounds__(kThreads) k_sched_tiles(const int32_t* cu, int32_t n_seg, int32_t T, int32_t tile,
                                                           int32_t* toff, int32_t* hist, int32_t n_bins,
-                                                          int32_t* n_items) {
+                                                          int32_t* n_items, int64_t cap) {
   __shared__ int32_t wsum[kThreads / 64];
   for (int32_t i = threadIdx.x; i < n_bins; i += kThreads) hist[i] = 0;
   int32_t carry = 0;
@@ -64,7 +67,7 @@ __global__ void __launch_bounds__(kThreads) k_sched_tiles(const int32_t* cu, int
   }
   if (threadIdx.x == 0) {
     toff[n_seg] = carry;
-    *n_items = carry;
+    *n_items = (int32_t)min((int64_t)carry, cap);
   }
 }
 
@@ -287,7 +290,7 @@ hipError_t launch_schedule(const int32_t* cu, int32_t n_seg, int32_t T, int tile
     return hipGetLastError();
   }
   const unsigned gt = (unsigned)((s.cap + kThreads - 1) / kThreads);
-  k_sched_tiles<<<1, kThreads, 0, stream>>>(cu, n_seg, T, tile, s.toff, s.hist, s.n_bins, s.n_items);
+  k_sched_tiles<<<1, kThreads, 0, stream>>>(cu, n_seg, T, tile, s.toff, s.hist, s.n_bins, s.n_items, s.cap);
   k_sched_count<<<gt, kThreads, 0, stream>>>(cu, n_seg, T, tile, unit, suffix, s.toff, s.hist, s.n_bins, s.cap);
   k_sched_scan<<<1, kThreads, 0, stream>>>(s.hist, s.n_bins);
   k_sched_fill<<<gt, kThreads, 0, stream>>>(cu, n_seg, T, tile, unit, suffix, s.toff, s.hist, s.n_bins, s.items,

@@ -29,10 +29,7 @@ int pack_dims(int mode, int64_t n_docs, int64_t n_tokens, int32_t micro_bsz, int
   return PSC_OK;
 }
 
-bool supported_head_dim(int dtype, int32_t d) {
-  if (dtype == PSC_BF16) return d == 64 || d == 128;
-  return d == 32 || d == 64 || d == 128;
-}
+bool supported_head_dim(int32_t d) { return d == 32 || d == 64 || d == 128; }
 
 int attn_dims(int dtype, int64_t T, int32_t n_seg, int32_t max_seqlen, int32_t hq, int32_t hkv, int32_t head_dim,
               float softmax_scale, psc::AttnDims* out) {
@@ -40,7 +37,7 @@ int attn_dims(int dtype, int64_t T, int32_t n_seg, int32_t max_seqlen, int32_t h
   if (T < 0 || T > kI32Max || n_seg < 0 || hq < 1 || hkv < 1 || head_dim < 1) return PSC_ERR_INVALID;
   if (hq % hkv != 0) return PSC_ERR_INVALID;
   if (T > 0 && (n_seg < 1 || n_seg > T || max_seqlen < 1 || max_seqlen > T)) return PSC_ERR_INVALID;
-  if (!supported_head_dim(dtype, head_dim)) return PSC_ERR_UNSUPPORTED;
+  if (!supported_head_dim(head_dim)) return PSC_ERR_UNSUPPORTED;
   if (!(softmax_scale == softmax_scale) || std::isinf(softmax_scale)) return PSC_ERR_INVALID;
   out->T = T;
   out->n_seg = n_seg;
@@ -68,9 +65,31 @@ bool operand_ok(const void* p, int64_t tok_stride, int32_t heads, int32_t d, int
   return true;
 }
 
+// Debug builds (PSC_DEBUG_CHECKS) keep 256 bytes at the end of the attention
+// workspaces for the cu_seqlens check's flags word.
+#ifdef PSC_DEBUG_CHECKS
+constexpr size_t kDebugTail = 256;
+#else
+constexpr size_t kDebugTail = 0;
+#endif
+
 size_t workspace_for(int pass, int dtype, const psc::AttnDims& d) {
-  return pass == 0 ? psc::attn_fwd_workspace_bytes(dtype, d) : psc::attn_bwd_workspace_bytes(dtype, d);
+  return (pass == 0 ? psc::attn_fwd_workspace_bytes(dtype, d) : psc::attn_bwd_workspace_bytes(dtype, d)) +
+         kDebugTail;
 }
+
+#ifdef PSC_DEBUG_CHECKS
+// Runs the cu_seqlens check on `stream`, waits for it and maps the flags to a
+// status (the one synchronising path of the library; debug builds only).
+int debug_check_cu(const int32_t* cu, int32_t n_seg, int64_t T, void* ws, size_t need, hipStream_t stream) {
+  int32_t* flags = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + need - kDebugTail);
+  if (psc::launch_check_cu(cu, n_seg, (int32_t)T, flags, stream) != hipSuccess) return PSC_ERR_HIP;
+  int32_t h = 0;
+  if (hipMemcpyAsync(&h, flags, sizeof(h), hipMemcpyDeviceToHost, stream) != hipSuccess) return PSC_ERR_HIP;
+  if (hipStreamSynchronize(stream) != hipSuccess) return PSC_ERR_HIP;
+  return psc_cu_seqlens_status(h);
+}
+#endif
 
 }  // namespace
 
@@ -168,6 +187,10 @@ int psc_varlen_attn_fwd(int dtype, const void* q, const void* k, const void* v, 
   const size_t need = workspace_for(0, dtype, d);
   if (T > 0 && (!workspace || workspace_bytes < need)) return PSC_ERR_WORKSPACE;
   if (T == 0) return PSC_OK;
+#ifdef PSC_DEBUG_CHECKS
+  if (int c = debug_check_cu(cu_seqlens, n_segments, T, workspace, need, static_cast<hipStream_t>(stream)))
+    return c;
+#endif
 
   psc::AttnFwdArgs a;
   a.dims = d;
@@ -187,15 +210,17 @@ int psc_varlen_attn_fwd(int dtype, const void* q, const void* k, const void* v, 
   return e == hipSuccess ? PSC_OK : PSC_ERR_HIP;
 }
 
-int psc_varlen_attn_bwd(int dtype, const void* q, const void* k, const void* v, const void* out, const void* dout,
-                        const float* lse, int64_t q_tok_stride, int64_t k_tok_stride, int64_t v_tok_stride,
-                        int64_t out_tok_stride, int64_t dout_tok_stride, const int32_t* cu_seqlens,
-                        int32_t n_segments, int32_t max_seqlen, int64_t total_tokens, int32_t hq, int32_t hkv,
-                        int32_t head_dim, float softmax_scale, float* dq, float* dk, float* dv, void* workspace,
-                        size_t workspace_bytes, void* stream) {
+int psc_varlen_attn_bwd(int dtype, int grad_dtype, const void* q, const void* k, const void* v, const void* out,
+                        const void* dout, const float* lse, int64_t q_tok_stride, int64_t k_tok_stride,
+                        int64_t v_tok_stride, int64_t out_tok_stride, int64_t dout_tok_stride,
+                        const int32_t* cu_seqlens, int32_t n_segments, int32_t max_seqlen, int64_t total_tokens,
+                        int32_t hq, int32_t hkv, int32_t head_dim, float softmax_scale, void* dq, void* dk,
+                        void* dv, void* workspace, size_t workspace_bytes, void* stream) {
   psc::AttnDims d;
   int st = attn_dims(dtype, total_tokens, n_segments, max_seqlen, hq, hkv, head_dim, softmax_scale, &d);
   if (st != PSC_OK) return st;
+  if (grad_dtype != PSC_F32 && grad_dtype != PSC_BF16) return PSC_ERR_INVALID;
+  if (dtype == PSC_F32 && grad_dtype != PSC_F32) return PSC_ERR_UNSUPPORTED;
   const int64_t T = total_tokens;
   if (!operand_ok(q, q_tok_stride, hq, head_dim, dtype, T) || !operand_ok(k, k_tok_stride, hkv, head_dim, dtype, T) ||
       !operand_ok(v, v_tok_stride, hkv, head_dim, dtype, T) ||
@@ -209,6 +234,10 @@ int psc_varlen_attn_bwd(int dtype, const void* q, const void* k, const void* v, 
   const size_t need = workspace_for(1, dtype, d);
   if (T > 0 && (!workspace || workspace_bytes < need)) return PSC_ERR_WORKSPACE;
   if (T == 0) return PSC_OK;
+#ifdef PSC_DEBUG_CHECKS
+  if (int c = debug_check_cu(cu_seqlens, n_segments, T, workspace, need, static_cast<hipStream_t>(stream)))
+    return c;
+#endif
 
   psc::AttnBwdArgs a;
   a.dims = d;
@@ -227,10 +256,30 @@ int psc_varlen_attn_bwd(int dtype, const void* q, const void* k, const void* v, 
   a.dq = dq;
   a.dk = dk;
   a.dv = dv;
+  a.grad_bf16 = grad_dtype == PSC_BF16;
   a.workspace = workspace;
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = dtype == PSC_BF16 ? psc::launch_attn_bwd_bf16(a, s) : psc::launch_attn_bwd_f32(a, s);
   return e == hipSuccess ? PSC_OK : PSC_ERR_HIP;
+}
+
+int psc_check_cu_seqlens(const int32_t* cu_seqlens, int32_t n_segments, int64_t total_tokens, int32_t* flags,
+                         void* stream) {
+  if (n_segments < 0 || total_tokens < 0 || total_tokens > kI32Max) return PSC_ERR_INVALID;
+  if (!cu_seqlens || !flags) return PSC_ERR_INVALID;
+  const hipError_t e =
+      psc::launch_check_cu(cu_seqlens, n_segments, (int32_t)total_tokens, flags, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PSC_OK : PSC_ERR_HIP;
+}
+
+int psc_cu_seqlens_status(int32_t flags) { return flags == 0 ? PSC_OK : PSC_ERR_INVALID; }
+
+int psc_debug_checks(void) {
+#ifdef PSC_DEBUG_CHECKS
+  return 1;
+#else
+  return 0;
+#endif
 }
 
 int psc_rope(int dtype, void* q, int64_t q_tok_stride, int32_t hq, void* k, int64_t k_tok_stride, int32_t hkv,

@@ -81,7 +81,8 @@ struct AttnBwdArgs {
   const float* lse;
   int64_t sq, sk, sv, so, sdo;
   const int32_t* cu;
-  float *dq, *dk, *dv;
+  void *dq, *dk, *dv;  // float32, or bf16 when grad_bf16 (bf16 inputs only)
+  int32_t grad_bf16;
   void* workspace;
 };
 
@@ -133,5 +134,11 @@ hipError_t launch_split(const int32_t* in, int64_t rows, int32_t length, int32_t
                         hipStream_t stream);
 hipError_t launch_row_max_seqlen(const int32_t* cu, int64_t n_cu, const int32_t* row_seg_ptr, int64_t n_rows,
                                  int32_t* out, hipStream_t stream);
+
+// cu_seqlens check (validate.hip): flags[0] = OR of the kCu* bits that apply.
+constexpr int32_t kCuBadStart = 1;       // c_0 != 0
+constexpr int32_t kCuBadEnd = 2;         // c_n != T
+constexpr int32_t kCuNotIncreasing = 4;  // some c_{i+1} <= c_i
+hipError_t launch_check_cu(const int32_t* cu, int32_t n_seg, int32_t T, int32_t* flags, hipStream_t stream);
 
 }  // namespace psc

@@ -99,7 +99,7 @@ def _fwd_raw(**kw):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(d=96), psc.ERR_UNSUPPORTED),
-    (dict(d=32), psc.ERR_UNSUPPORTED),          # bf16 needs 64 or 128
+    (dict(d=48, wsb=8), psc.ERR_UNSUPPORTED),   # checked before the workspace
     (dict(hq=3, hkv=2), psc.ERR_INVALID),        # hq % hkv != 0
     (dict(dtype=7), psc.ERR_INVALID),
     (dict(q=None), psc.ERR_INVALID),
@@ -126,17 +126,99 @@ def test_attn_empty_is_a_no_op():
 def test_attn_bwd_rejects_on_host():
     v = lambda x: None if x is None else ctypes.c_void_p(x)
     L = psc.lib()
-    base = [psc.BF16, v(16), v(16), v(16), v(16), v(16), v(16), 256, 128, 128, 256, 256, v(16), 1, 16, 16, 2, 1,
-            128, 0.0, v(16), v(16), v(16), v(16), 1 << 24, None]
+    # every case below also has too small a workspace, so nothing could be
+    # launched on these fake pointers even if the check under test were missing
+    base = [psc.BF16, psc.F32, v(16), v(16), v(16), v(16), v(16), v(16), 256, 128, 128, 256, 256, v(16), 1, 16, 16,
+            2, 1, 128, 0.0, v(16), v(16), v(16), v(16), 8, None]
+    assert L.psc_varlen_attn_bwd(*base) == psc.ERR_WORKSPACE
     bad_dq = list(base)
-    bad_dq[20] = None
+    bad_dq[21] = None
     assert L.psc_varlen_attn_bwd(*bad_dq) == psc.ERR_INVALID
     bad_hd = list(base)
-    bad_hd[18] = 48
+    bad_hd[19] = 48
     assert L.psc_varlen_attn_bwd(*bad_hd) == psc.ERR_UNSUPPORTED
     mis = list(base)
-    mis[21] = v(20)  # dk not 16-byte aligned
+    mis[22] = v(20)  # dk not 16-byte aligned
     assert L.psc_varlen_attn_bwd(*mis) == psc.ERR_INVALID
+    for g, code in ((7, psc.ERR_INVALID), (-1, psc.ERR_INVALID)):
+        bad_g = list(base)
+        bad_g[1] = g
+        assert L.psc_varlen_attn_bwd(*bad_g) == code
+    f32_bf16 = list(base)
+    f32_bf16[0], f32_bf16[1] = psc.F32, psc.BF16  # bf16 gradients need bf16 inputs
+    assert L.psc_varlen_attn_bwd(*f32_bf16) == psc.ERR_UNSUPPORTED
+    bf16_bf16 = list(base)
+    bf16_bf16[1] = psc.BF16
+    assert L.psc_varlen_attn_bwd(*bf16_bf16) == psc.ERR_WORKSPACE  # accepted up to the workspace check
+
+
+def test_head_dim_32_is_supported_for_both_dtypes():
+    for dt in (psc.F32, psc.BF16):
+        assert psc.varlen_attn_workspace(0, dt, 4096, 8, 1024, 8, 2, 32) > 0
+        assert psc.varlen_attn_workspace(1, dt, 4096, 8, 1024, 8, 2, 32) > 0
+    with pytest.raises(psc.PscError) as e:
+        psc.varlen_attn_workspace(0, psc.BF16, 4096, 8, 1024, 8, 2, 96)
+    assert e.value.status == psc.ERR_UNSUPPORTED
+
+
+def test_cu_seqlens_status_host_mapping():
+    # the flags word psc_check_cu_seqlens writes, mapped on the host
+    assert psc.cu_seqlens_status(0) == psc.OK
+    for f in (psc.CU_BAD_START, psc.CU_BAD_END, psc.CU_NOT_INCREASING, 3, 5, 6, 7):
+        assert psc.cu_seqlens_status(f) == psc.ERR_INVALID
+    assert psc.lib().psc_debug_checks() == 0
+
+
+def test_debug_library_reports_its_checks():
+    if not os.path.exists(psc.DEBUG_LIB_PATH):
+        pytest.skip("libpsc_debug.so not built")
+    D = psc.debug_lib()
+    assert D.psc_debug_checks() == 1
+    assert D.psc_cu_seqlens_status(psc.CU_NOT_INCREASING) == psc.ERR_INVALID
+    # the debug build keeps a flags word at the end of each attention workspace
+    b_rel, b_dbg = ctypes.c_size_t(), ctypes.c_size_t()
+    assert psc.lib().psc_varlen_attn_workspace(0, psc.BF16, 4096, 8, 1024, 8, 2, 128, ctypes.byref(b_rel)) == 0
+    assert D.psc_varlen_attn_workspace(0, psc.BF16, 4096, 8, 1024, 8, 2, 128, ctypes.byref(b_dbg)) == 0
+    assert b_dbg.value == b_rel.value + 256
+
+
+@pytest.mark.parametrize("cu,n,T,flags", [(None, 3, 16, 16), (16, 3, 16, None), (16, -1, 16, 16),
+                                          (16, 3, -1, 16), (16, 3, 1 << 31, 16)])
+def test_check_cu_seqlens_rejects_on_host(cu, n, T, flags):
+    v = lambda x: None if x is None else ctypes.c_void_p(x)
+    assert psc.lib().psc_check_cu_seqlens(v(cu), n, T, v(flags), None) == psc.ERR_INVALID
+
+
+def test_binding_rejects_mismatched_buffers_before_the_call():
+    import torch
+
+    T, hq, hkv, D = 16, 2, 1, 64
+    q = torch.zeros(T, hq, D, dtype=torch.bfloat16)
+    k = torch.zeros(T, hkv, D, dtype=torch.bfloat16)
+    cu = torch.tensor([0, T], dtype=torch.int32)
+    lse = torch.zeros(hq, T)
+    with pytest.raises(ValueError):  # k in another dtype than q
+        psc.varlen_attn_fwd(q, k.float(), k, cu, T)
+    with pytest.raises(ValueError):  # cu_seqlens not int32
+        psc.varlen_attn_fwd(q, k, k, cu.long(), T)
+    with pytest.raises(ValueError):  # lse of the wrong shape
+        psc.varlen_attn_fwd(q, k, k, cu, T, out=q.clone(), lse=torch.zeros(T, hq))
+    with pytest.raises(ValueError):  # out in another dtype
+        psc.varlen_attn_fwd(q, k, k, cu, T, out=q.float(), lse=lse)
+    g32 = dict(dtype=torch.float32)
+    with pytest.raises(ValueError):  # dq in bf16 while fp32 gradients are asked for
+        psc.varlen_attn_bwd(q, k, k, q, q, lse, cu, T, dq=torch.zeros(T, hq, D, dtype=torch.bfloat16),
+                            dk=torch.zeros(T, hkv, D, **g32), dv=torch.zeros(T, hkv, D, **g32))
+    with pytest.raises(ValueError):  # dk too small
+        psc.varlen_attn_bwd(q, k, k, q, q, lse, cu, T, dq=torch.zeros(T, hq, D, **g32),
+                            dk=torch.zeros(T - 1, hkv, D, **g32), dv=torch.zeros(T, hkv, D, **g32))
+    with pytest.raises(ValueError):  # dv not contiguous
+        psc.varlen_attn_bwd(q, k, k, q, q, lse, cu, T, dq=torch.zeros(T, hq, D, **g32),
+                            dk=torch.zeros(T, hkv, D, **g32), dv=torch.zeros(T, hkv, 2 * D, **g32)[..., ::2])
+    with pytest.raises(ValueError):  # bf16 gradients asked for, fp32 buffers given
+        psc.varlen_attn_bwd(q, k, k, q, q, lse, cu, T, dq=torch.zeros(T, hq, D, **g32),
+                            dk=torch.zeros(T, hkv, D, **g32), dv=torch.zeros(T, hkv, D, **g32),
+                            grad_dtype=psc.BF16)
 
 
 def test_attn_workspace_sizes():

@@ -1,13 +1,19 @@
 """GPU document-causal attention vs the fp64 oracle.
 
-Tolerances: fp32 inputs max-abs 1e-5; bf16 inputs max-abs 2e-2 and rel-L2
-(||x - ref|| / ||ref|| over the compared elements) <= 5e-3, on O, lse, dQ, dK
-and dV.  Small cases compare every element against the full oracle; the
-full-size workloads, run exactly as the benchmark launches them, compare
-sampled outputs that the oracle computes one by one (random and tail rows of
-O / lse / dQ, the key tail of the longest document and whole short documents
-for dK / dV).  Also: results repeat bit for bit, writes stay inside their
-buffers (guard bands), and k / v may be strided views of one packed kv buffer.
+Tolerances, one bar for every case: fp32 inputs max-abs 1e-5; bf16 inputs
+max-abs 2e-2 and rel-L2 (||x - ref|| / ||ref|| over the compared elements)
+<= 5e-3, on O, lse, dQ, dK and dV.  Gradients stored in bf16 carry their
+storage rounding on top: per element, half a bf16 ulp of the stored value is
+added to the max-abs bar (the fp32 gradients of the same kernels are checked
+to round to them exactly).  Small cases compare every element against the full
+oracle; the full-size workloads, run exactly as the benchmark launches them,
+compare sampled outputs that the oracle computes one by one: random rows and
+the last 64 rows of every long document (O, lse, dQ), the first 128 and the
+last keys of the longest document and whole short documents (dK, dV).  Also:
+results repeat bit for bit, writes stay inside their buffers (guard bands),
+k / v may be strided views of one packed kv buffer, and a non-default stream
+is honoured.  Cases outside the stated bar (a sharper softmax, 8 query heads
+per key/value head) are strict expected failures with their measured error.
 """
 import numpy as np
 import pytest
@@ -23,24 +29,44 @@ BF16_MAX_ABS, BF16_REL_L2 = 2e-2, 5e-3
 F32_MAX_ABS = 1e-5
 
 
-def close(name, got, ref, dtype, max_abs=BF16_MAX_ABS):
+def half_ulp_bf16(x):
+    """Half a bf16 ulp at |x| (8 significant bits): 2^(floor(log2|x|) - 8),
+    and 0 at x = 0."""
+    a = np.abs(np.asarray(x, dtype=np.float64))
+    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    return np.where(a > 0, np.ldexp(1.0, (e - 8).astype(np.int64)), 0.0)
+
+
+def close(name, got, ref, dtype, stored_bf16=False):
     got = np.asarray(got, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
     assert got.shape == ref.shape, (name, got.shape, ref.shape)
     assert np.isfinite(got).all(), name
     err = np.abs(got - ref)
-    mx = float(err.max()) if err.size else 0.0
     if dtype == "f32":
+        mx = float(err.max()) if err.size else 0.0
         assert mx <= F32_MAX_ABS, f"{name}: max-abs {mx:.3e}"
         return
+    # a value stored in bf16 also carries its own rounding: half an ulp of the
+    # stored value, on top of the bar
+    if stored_bf16:
+        err = err - half_ulp_bf16(np.maximum(np.abs(got), np.abs(ref)))
+    mx = float(err.max()) if err.size else 0.0
     # rel-L2 is undefined against an all-zero reference (e.g. dq and dk of
     # one-token documents are exactly 0); max-abs alone governs there
     nref = float(np.linalg.norm(ref))
     rel = float(np.linalg.norm(got - ref) / nref) if nref > 0 else 0.0
-    assert mx <= max_abs and rel <= BF16_REL_L2, f"{name}: max-abs {mx:.3e} rel-L2 {rel:.3e}"
+    assert mx <= BF16_MAX_ABS and rel <= BF16_REL_L2, f"{name}: max-abs {mx:.3e} rel-L2 {rel:.3e}"
 
 
-def run(q, k, v, do, cu, backward=True, scale=None):
+def errors(got, ref):
+    """(max-abs, rel-L2) of got against ref, for reporting."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    return float(np.abs(got - ref).max()), float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-300))
+
+
+def run(q, k, v, do, cu, backward=True, scale=None, grad_dtype=None):
     dev = torch.device("cuda:0")
     qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
     cud = torch.as_tensor(np.asarray(cu, dtype=np.int32)).to(dev)
@@ -48,28 +74,24 @@ def run(q, k, v, do, cu, backward=True, scale=None):
     out, lse = psc.varlen_attn_fwd(qd, kd, vd, cud, maxlen, softmax_scale=scale)
     res = {"o": out, "lse": lse}
     if backward:
-        dq, dk, dv = psc.varlen_attn_bwd(qd, kd, vd, out, do.to(dev), lse, cud, maxlen, softmax_scale=scale)
+        dq, dk, dv = psc.varlen_attn_bwd(qd, kd, vd, out, do.to(dev), lse, cud, maxlen, softmax_scale=scale,
+                                         grad_dtype=grad_dtype)
         res.update(dq=dq, dk=dk, dv=dv)
     torch.cuda.synchronize()
-    return {key: val.float().cpu() for key, val in res.items()}
+    return {key: val.cpu() for key, val in res.items()}
 
 
-def full_compare(q, k, v, do, cu, dtype, backward=True, scale=None):
-    got = run(q, k, v, do, cu, backward, scale)
+def full_compare(q, k, v, do, cu, dtype, backward=True, scale=None, grad_dtype=None):
+    got = run(q, k, v, do, cu, backward, scale, grad_dtype)
     o, lse = attn_ref.attn_fwd(q, k, v, cu, softmax_scale=scale)
-    close("o", got["o"], o, dtype)
+    close("o", got["o"].float(), o, dtype)
     close("lse", got["lse"], lse, dtype)
     if backward:
         dq, dk, dv = attn_ref.attn_bwd(q, k, v, do, cu, softmax_scale=scale)
-        close("dq", got["dq"], dq, dtype)
-        # dK and dV sum the contributions of the G = hq / hkv query heads of
-        # their key/value head, each carrying the bf16 rounding of P and dS;
-        # the 2e-2 bar is the one stated for the workloads (G <= 4) and scales
-        # by G / 4 beyond that (rel-L2 keeps its bar)
-        g = q.shape[1] // k.shape[1]
-        kv_abs = BF16_MAX_ABS * max(1.0, g / 4)
-        close("dk", got["dk"], dk, dtype, kv_abs)
-        close("dv", got["dv"], dv, dtype, kv_abs)
+        sb = grad_dtype == psc.BF16
+        close("dq", got["dq"].float(), dq, dtype, sb)
+        close("dk", got["dk"].float(), dk, dtype, sb)
+        close("dv", got["dv"].float(), dv, dtype, sb)
     return got
 
 
@@ -98,7 +120,18 @@ def test_fp32_random_layouts(hq, hkv, D, seed):
 EDGE_LAYOUT = [1, 63, 64, 65, 127, 128, 129, 1, 1, 200, 300, 431]
 
 
-@pytest.mark.parametrize("hq,hkv,D", [(8, 2, 128), (4, 4, 64), (4, 1, 128), (6, 3, 64)])
+# Measured above the bar (deterministic kernels, fixed inputs): strict expected
+# failures, so a change that moves them either way is noticed.
+OVER_BAR_D32_G4 = pytest.mark.xfail(
+    strict=True, reason="outside the stated bar: head_dim 32 with 4 query heads per key/value head, dK max-abs "
+                        "2.008e-2 (rel-L2 1.9e-3) from the bf16 rounding of dS summed over the group's heads")
+OVER_BAR_G8 = pytest.mark.xfail(
+    strict=True, reason="outside the stated bar: 8 query heads per key/value head at D 128, dV max-abs 2.069e-2 "
+                        "(rel-L2 1.6e-3) from the bf16 rounding of P summed over the group's heads")
+
+
+@pytest.mark.parametrize("hq,hkv,D", [(8, 2, 128), (4, 4, 64), (4, 1, 128), (6, 3, 64),
+                                      pytest.param(8, 2, 32, marks=OVER_BAR_D32_G4), (3, 3, 32)])
 def test_bf16_edge_layout(hq, hkv, D):
     cu = np.concatenate([[0], np.cumsum(EDGE_LAYOUT)]).astype(np.int32)
     T = int(cu[-1])
@@ -109,8 +142,12 @@ def test_bf16_edge_layout(hq, hkv, D):
 # Query-head groups the forward and dQ pack differently: 8 heads per key/value
 # head (two 4-head workgroups per group), 2 (64-row x 2-head tiles) and odd
 # groups of 3 and 5 (128-row x 1-head tiles), on lengths around the 32-, 64-
-# and 128-row tile edges.
-@pytest.mark.parametrize("hq,hkv,D", [(16, 2, 128), (8, 1, 64), (4, 2, 128), (6, 2, 128), (5, 1, 64)])
+# and 128-row tile edges.  Groups above 4 query heads per key/value head lie
+# outside the stated bar (dK and dV sum the bf16 rounding of P and dS over
+# every head of the group); they are strict expected failures where measured
+# above it.
+@pytest.mark.parametrize("hq,hkv,D", [pytest.param(16, 2, 128, marks=OVER_BAR_G8), (8, 1, 64), (4, 2, 128),
+                                      (6, 2, 128), (5, 1, 64), (8, 4, 32), (4, 2, 32)])
 def test_bf16_head_groups(hq, hkv, D):
     lens = [31, 32, 33, 1, 96, 97, 160, 255, 64, 300]
     cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
@@ -151,10 +188,19 @@ def test_bf16_mixed_layout_sweep(seed):
     full_compare(q, k, v, do, cu, "bf16")
 
 
-@pytest.mark.parametrize("factor", [0.5, 1.25])
+@pytest.mark.parametrize("factor", [
+    0.5, 1.25, 1.5,
+    pytest.param(1.75, marks=pytest.mark.xfail(
+        strict=True, reason="outside the stated bar (softmax_scale above 1.5/sqrt(D)): dK max-abs 3.12e-2, "
+                            "dQ 2.36e-2 (rel-L2 2.1e-3) from the bf16 rounding of dS")),
+    pytest.param(0.2 * np.sqrt(128), marks=pytest.mark.xfail(
+        strict=True, reason="outside the stated bar: softmax_scale 0.2 at D 128 (2.26/sqrt(D)), dK max-abs "
+                            "3.20e-2, dQ 2.76e-2 (rel-L2 2.3e-3) from the bf16 rounding of dS")),
+])
 def test_bf16_explicit_softmax_scale(factor):
-    # the scale argument is honoured (a factor around the default 1/sqrt(D));
-    # much sharper softmax than this grows the bf16 rounding error of dS in dQ
+    # the scale argument is honoured; the bar holds up to 1.5/sqrt(D), the
+    # range psc.h states, and a sharper softmax grows the bf16 rounding of dS
+    # in dQ and dK beyond it
     rng = np.random.default_rng(77)
     T, D = 1500, 128
     cu = workloads.random_layout(rng, T, 1, 700)
@@ -242,32 +288,46 @@ def _layout(w):
     return np.asarray(pack_ref.flatten(rows, p.packed_length)["cu_seqlens"], dtype=np.int32)
 
 
-def sampled_check(q, k, v, do, cu, a_hq, a_hkv, dtype, backward, got, seed=1):
-    """Sampled comparison with the oracle at full size: random rows and the
-    tail of the longest document (o, lse, dq), the last keys of the longest
-    document (dk, dv for one kv head) and two whole short documents."""
+def sampled_check(q, k, v, do, cu, a_hq, a_hkv, dtype, backward, got, seed=1, head_kv=2):
+    """Sampled comparison with the oracle at full size.
+
+    O, lse and dQ: 192 random (row, head) pairs plus the last 64 rows of each
+    of the (up to 8) longest documents of at least 512 tokens, heads drawn at
+    random.  dK, dV: the first 128 keys of the longest document for `head_kv`
+    key/value heads (those keys sum over every later row of the document and
+    every query head of the group: the most accumulated terms), its last 160
+    keys for one head, and two whole short documents for every head."""
     T = int(cu[-1])
     rng = np.random.default_rng(seed)
     lens = np.diff(cu)
     longest = int(np.argmax(lens))
     s_long, e_long = int(cu[longest]), int(cu[longest + 1])
-    rows = np.concatenate([rng.integers(0, T, 96), np.arange(e_long - 32, e_long)])
+    long_docs = [int(i) for i in np.argsort(-lens, kind="stable") if lens[i] >= 512][:8]
+    tails = [np.arange(int(cu[i + 1]) - 64, int(cu[i + 1])) for i in long_docs]
+    rows = np.concatenate([rng.integers(0, T, 192)] + tails)
     heads = rng.integers(0, a_hq, rows.size)
     o, lse = attn_ref.attn_rows(q, k, v, cu, rows, heads)
-    close("o", got["o"][rows, heads].numpy(), o, dtype)
+    close("o", got["o"][rows, heads].float().numpy(), o, dtype)
     close("lse", got["lse"][heads, rows].numpy(), lse, dtype)
     if not backward:
         return
-    dq = attn_ref.attn_rows_dq(q, k, v, do, cu, rows[:64], heads[:64])
-    close("dq", got["dq"][rows[:64], heads[:64]].numpy(), dq, dtype)
+    dq = attn_ref.attn_rows_dq(q, k, v, do, cu, rows, heads)
+    close(f"dq ({rows.size} rows)", got["dq"][rows, heads].numpy(), dq, dtype)
+    kvs = sorted(int(g) for g in rng.choice(a_hkv, min(head_kv, a_hkv), replace=False))
+    key_hi = min(e_long, s_long + 128)
+    print(f"  dk/dv head keys [{s_long}, {key_hi}) of the {e_long - s_long}-token document, kv heads {kvs}",
+          flush=True)
+    dk, dv = attn_ref.attn_bwd_keys(q, k, v, do, cu, longest, s_long, kvs, key_hi=key_hi)
+    close("dk head", got["dk"][s_long:key_hi][:, kvs].numpy(), dk, dtype)
+    close("dv head", got["dv"][s_long:key_hi][:, kvs].numpy(), dv, dtype)
     g = int(rng.integers(0, a_hkv))
     key_lo = max(s_long, e_long - 160)
     dk, dv = attn_ref.attn_bwd_keys(q, k, v, do, cu, longest, key_lo, [g])
     close("dk tail", got["dk"][key_lo:e_long, [g]].numpy(), dk, dtype)
     close("dv tail", got["dv"][key_lo:e_long, [g]].numpy(), dv, dtype)
-    short = [i for i in np.argsort(lens) if lens[i] > 8][:2]
     if len(lens) < 2:
         return
+    short = [i for i in np.argsort(lens, kind="stable") if lens[i] > 8][:2]
     heads_kv = list(range(a_hkv))
     for si in short:
         s, e = int(cu[si]), int(cu[si + 1])
@@ -287,7 +347,7 @@ def test_full_size_sampled(name):
     q, k, v, do = workloads.qkv_do(T, a.hq, a.hkv, a.head_dim, seed=0, dtype=a.dtype)
     print(f"[{name}] T={T} segments={len(cu) - 1} hq={a.hq} hkv={a.hkv} D={a.head_dim}", flush=True)
     got = run(q, k, v, do, cu, backward=a.backward)
-    sampled_check(q, k, v, do, cu, a.hq, a.hkv, a.dtype, a.backward, got)
+    sampled_check(q, k, v, do, cu, a.hq, a.hkv, a.dtype, a.backward, got, head_kv=4 if a.hq == a.hkv else 2)
 
 
 # The document-length sweep's rows (one 32768-token row, GQA 32/8, D 128):
@@ -300,4 +360,104 @@ def test_doc_sweep_layouts_sampled(name, whole_row):
     q, k, v, do = workloads.qkv_do(T, 32, 8, 128, seed=0, dtype="bf16")
     print(f"[sweep {name} whole_row={whole_row}] T={T} segments={len(cu) - 1}", flush=True)
     got = run(q, k, v, do, cu, backward=True)
-    sampled_check(q, k, v, do, cu, 32, 8, "bf16", True, got)
+    sampled_check(q, k, v, do, cu, 32, 8, "bf16", True, got, head_kv=1)
+
+
+# ------------------------------------------------ bf16 gradients, streams
+
+@pytest.mark.parametrize("hq,hkv,D", [(8, 2, 128), (4, 4, 64), (4, 2, 32)])
+def test_bf16_gradients(hq, hkv, D):
+    # gradients stored in bf16: within the bar plus their own storage rounding
+    # against the oracle, and equal to the fp32 gradients of the same kernels
+    # rounded to nearest even (each is rounded once, from the fp32 accumulator)
+    lens = [1, 63, 64, 65, 200, 431, 7]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    T = int(cu[-1])
+    q, k, v, do = workloads.qkv_do(T, hq, hkv, D, seed=31 + D, dtype="bf16")
+    got = full_compare(q, k, v, do, cu, "bf16", grad_dtype=psc.BF16)
+    f32 = run(q, k, v, do, cu)
+    for name in ("dq", "dk", "dv"):
+        assert got[name].dtype == torch.bfloat16
+        assert torch.equal(got[name], f32[name].to(torch.bfloat16)), name
+
+
+def test_bf16_gradients_at_full_size_round_the_fp32_ones():
+    w = workloads.make("lognormal_32k")
+    cu = _layout(w)
+    T = int(cu[-1])
+    a = w.attn
+    q, k, v, do = workloads.qkv_do(T, a.hq, a.hkv, a.head_dim, seed=0, dtype=a.dtype)
+    g32 = run(q, k, v, do, cu)
+    g16 = run(q, k, v, do, cu, grad_dtype=psc.BF16)
+    for name in ("dq", "dk", "dv"):
+        assert torch.equal(g16[name], g32[name].to(torch.bfloat16)), name
+
+
+def test_non_default_stream():
+    # every launch goes on the given stream, and the binding allocates its
+    # outputs and workspaces there: the results match the default-stream ones
+    cu = np.concatenate([[0], np.cumsum(EDGE_LAYOUT)]).astype(np.int32)
+    T, hq, hkv, D = int(cu[-1]), 8, 2, 128
+    q, k, v, do = workloads.qkv_do(T, hq, hkv, D, seed=12, dtype="bf16")
+    dev = torch.device("cuda:0")
+    qd, kd, vd, dod = q.to(dev), k.to(dev), v.to(dev), do.to(dev)
+    cud = torch.as_tensor(cu).to(dev)
+    ref = run(q, k, v, do, cu)
+    torch.cuda.synchronize()
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    o, lse = psc.varlen_attn_fwd(qd, kd, vd, cud, 431, stream=st)
+    dq, dk, dv = psc.varlen_attn_bwd(qd, kd, vd, o, dod, lse, cud, 431, stream=st)
+    st.synchronize()
+    for name, x in (("o", o), ("lse", lse), ("dq", dq), ("dk", dk), ("dv", dv)):
+        assert torch.equal(x.cpu(), ref[name]), name
+
+
+# -------------------------------------------------- cu_seqlens device check
+
+@pytest.mark.parametrize("cu,T,flags", [
+    ([0, 3, 7, 12, 16], 16, 0),
+    ([0, 16], 16, 0),
+    ([1, 3, 7, 12, 16], 16, psc.CU_BAD_START),
+    ([0, 3, 7, 12, 15], 16, psc.CU_BAD_END),
+    ([0, 3, 3, 12, 16], 16, psc.CU_NOT_INCREASING),
+    ([0, 7, 3, 12, 16], 16, psc.CU_NOT_INCREASING),
+    ([2, 9, 3, 12, 17], 16, psc.CU_BAD_START | psc.CU_BAD_END | psc.CU_NOT_INCREASING),
+    (list(range(0, 3001, 3)), 3000, 0),
+    (list(range(0, 3001, 3))[:-1] + [2997], 3000, psc.CU_BAD_END | psc.CU_NOT_INCREASING),
+])
+def test_check_cu_seqlens_flags(cu, T, flags):
+    cud = torch.tensor(cu, dtype=torch.int32, device="cuda:0")
+    got = int(psc.check_cu_seqlens(cud, T).item())
+    assert got == flags
+    assert psc.cu_seqlens_status(got) == (psc.OK if flags == 0 else psc.ERR_INVALID)
+
+
+def test_debug_library_rejects_bad_cu_seqlens_before_launch():
+    import os
+
+    if not os.path.exists(psc.DEBUG_LIB_PATH):
+        pytest.skip("libpsc_debug.so not built")
+    D = psc.debug_lib()
+    T, hq, hkv, hd = 16, 2, 1, 64
+    q, k, v, do = workloads.qkv_do(T, hq, hkv, hd, seed=3, dtype="bf16")
+    dev = torch.device("cuda:0")
+    qd, kd, vd, dod = q.to(dev), k.to(dev), v.to(dev), do.to(dev)
+    good = torch.tensor([0, 3, 7, 12, 16], dtype=torch.int32, device=dev)
+    o, lse = psc.varlen_attn_fwd(qd, kd, vd, good, 5, library=D)
+    dq, dk, dv = psc.varlen_attn_bwd(qd, kd, vd, o, dod, lse, good, 5, library=D)
+    torch.cuda.synchronize()
+    ref = run(q, k, v, do, [0, 3, 7, 12, 16])
+    assert torch.equal(o.cpu(), ref["o"]) and torch.equal(dq.cpu(), ref["dq"])
+    sentinel = torch.full_like(o, 7.0)
+    for bad in ([0, 3, 3, 12, 16], [0, 3, 7, 12, 15], [1, 3, 7, 12, 16]):
+        cu = torch.tensor(bad, dtype=torch.int32, device=dev)
+        out = sentinel.clone()
+        with pytest.raises(psc.PscError) as e:
+            psc.varlen_attn_fwd(qd, kd, vd, cu, 9, out=out, library=D)
+        assert e.value.status == psc.ERR_INVALID
+        with pytest.raises(psc.PscError) as e:
+            psc.varlen_attn_bwd(qd, kd, vd, o, dod, lse, cu, 9, library=D)
+        assert e.value.status == psc.ERR_INVALID
+        torch.cuda.synchronize()
+        assert torch.equal(out, sentinel)  # nothing was launched
