@@ -28,6 +28,8 @@
 // The streamed operand of each kernel (K/V blocks for dQ, Q/dO blocks plus
 // their lse and D for dK/dV) is double-buffered in LDS and filled with
 // asynchronous direct-to-LDS loads, as in the forward (attn_common.h).
+#include <type_traits>
+
 #include "attn_common.h"
 #include "psc_internal.h"
 
@@ -48,13 +50,13 @@ struct BwdParams {
   float* Dbuf;   // [hq][T]  -D_i
   float* NLbuf;  // [hq][T]  -lse_i / scale
   void *dq, *dk, *dv;  // float32, or bf16 when grad_bf16
-  int32_t grad_bf16;
   int64_t sq, sk, sv, so, sdo, T;
   const int32_t* cu;
   const int32_t* items;
   const int32_t* n_items;
   int32_t hq, hkv, group;
   float scale, scale_log2;
+  int32_t grad_bf16;  // launch selection only: the kernels take it as a template parameter
 };
 
 // ---------------------------------------------------------------------- dQ
@@ -160,7 +162,9 @@ __device__ __forceinline__ void dq_block(DqState<D>& st, const char* Ks, const c
 // DR = D / 2 runs heads of DR columns in the D-column kernel (as in the
 // forward): Q and dO are zero past DR in registers, so S, dP and D_i are those
 // of the head's columns, and only dQ's first DR columns are stored.
-template <int D, int HP, int DR = D>
+// GB: dQ stored in bf16 (else fp32); a template parameter so the fp32
+// kernel's code and registers are those of a kernel with no bf16 path.
+template <int D, int HP, int DR = D, bool GB = false>
 __global__ void __launch_bounds__(kThreads, 2) k_bwd_dq(BwdParams p) {
   static_assert(DR == D || 2 * DR == D, "a head fills the tile or half of it");
   constexpr int RW = kBQ / HP;  // query rows per workgroup
@@ -177,15 +181,15 @@ __global__ void __launch_bounds__(kThreads, 2) k_bwd_dq(BwdParams p) {
   const int hw = w % HP, rs = w / HP;
   const int32_t head = (int32_t)hg * HP + hw;
   // item < cap (the grid is cap work-groups per head group), so the entry is read
-  // together with the count and used only once the count admits it, and
-  // clamped to the token range (tile_item): a malformed cu_seqlens cannot
-  // send any access outside the tensors.
+  // together with the count and used only once the count admits it.  The
+  // schedule writes every entry below the count, with segment bounds clamped
+  // to [0, T]: a malformed cu_seqlens cannot send any access outside the
+  // tensors.
   const int4 it = *reinterpret_cast<const int4*>(p.items + 4 * item);
   if ((int32_t)item >= *p.n_items) return;
-  TileItem ti;
-  if (!tile_item(it, p.T, RW, ti)) return;
-  const int32_t s0 = ti.s0, L = ti.L, tile = ti.tile;
+  const int32_t s0 = it.x, L = it.y, tile = it.z;
   const int32_t q0 = tile * RW;
+  if (q0 >= L) return;
   const int32_t kvh = (int32_t)hg * HP / p.group;
 
   const bf16* Kp = p.k + (int64_t)s0 * p.sk + (int64_t)kvh * DR;
@@ -267,7 +271,7 @@ __global__ void __launch_bounds__(kThreads, 2) k_bwd_dq(BwdParams p) {
   // time.  Inside a staged row, 16-byte chunk c sits at slot c ^ (row % kPC).
   char* const stage = (nkv & 1) ? (w < 2 ? Ks1 : Vs1) : (w < 2 ? Ks0 : Vs0);
   char* const ob = stage + (w & 1) * (tile_bytes<D>() / 2);
-  if (p.grad_bf16) {
+  if constexpr (GB) {
     // bf16 dQ: whole 2*D-byte rows fit half a tile at once (as the forward's O)
     constexpr int kChunks = D / 8;
     bf16* const dq = static_cast<bf16*>(p.dq);
@@ -539,7 +543,7 @@ __device__ __forceinline__ void dkdv_block_full(DkvState<D>& st, const char* Qs,
 // DR = D / 2 runs heads of DR columns: K and V are zero past DR in registers
 // (S and dP are those of the head's columns), and only the first DR columns of
 // dK and dV are stored.
-template <int D, int DR = D>
+template <int D, int DR = D, bool GB = false>
 __global__ void __launch_bounds__(kThreads, 2) k_bwd_dkdv(BwdParams p) {
   static_assert(D == 64, "k_bwd_dkdv8 handles D = 128");
   static_assert(DR == D || 2 * DR == D, "a head fills the tile or half of it");
@@ -555,15 +559,15 @@ __global__ void __launch_bounds__(kThreads, 2) k_bwd_dkdv(BwdParams p) {
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, h = l >> 5, lq = l & 31;
   const uint32_t item = blockIdx.x / (uint32_t)p.hkv, kvh = blockIdx.x % (uint32_t)p.hkv;
   // item < cap (the grid is cap work-groups per head), so the entry is read
-  // together with the count and used only once the count admits it, and
-  // clamped to the token range (tile_item): a malformed cu_seqlens cannot
-  // send any access outside the tensors.
+  // together with the count and used only once the count admits it.  The
+  // schedule writes every entry below the count, with segment bounds clamped
+  // to [0, T]: a malformed cu_seqlens cannot send any access outside the
+  // tensors.
   const int4 it = *reinterpret_cast<const int4*>(p.items + 4 * item);
   if ((int32_t)item >= *p.n_items) return;
-  TileItem ti;
-  if (!tile_item(it, p.T, kBKV, ti)) return;
-  const int32_t s0 = ti.s0, L = ti.L, tile = ti.tile;
+  const int32_t s0 = it.x, L = it.y, tile = it.z;
   const int32_t kb = tile * kBKV;
+  if (kb >= L) return;
   const int32_t key = kb + 32 * w + lq;  // this lane's key (S layout: lane <-> key)
   const bool kvalid = key < L;
   const int32_t wk_lo = kb + 32 * w;
@@ -635,16 +639,13 @@ __global__ void __launch_bounds__(kThreads, 2) k_bwd_dkdv(BwdParams p) {
   for (int i = 0; i < 16; ++i) {
     const int32_t kr = wk_lo + 8 * (i >> 2) + 4 * h + (i & 3);
     if (kr < L) {
-      const int64_t row = ((int64_t)(s0 + kr) * p.hkv + kvh) * DR;
+      using G = typename std::conditional<GB, bf16, float>::type;
+      G* dkr = static_cast<G*>(p.dk) + ((int64_t)(s0 + kr) * p.hkv + kvh) * DR;
+      G* dvr = static_cast<G*>(p.dv) + ((int64_t)(s0 + kr) * p.hkv + kvh) * DR;
 #pragma unroll
       for (int dt = 0; dt < DR / 32; ++dt) {
-        if (p.grad_bf16) {
-          static_cast<bf16*>(p.dk)[row + 32 * dt + lq] = (bf16)(st.dka[dt][i] * p.scale);
-          static_cast<bf16*>(p.dv)[row + 32 * dt + lq] = (bf16)st.dva[dt][i];
-        } else {
-          static_cast<float*>(p.dk)[row + 32 * dt + lq] = st.dka[dt][i] * p.scale;
-          static_cast<float*>(p.dv)[row + 32 * dt + lq] = st.dva[dt][i];
-        }
+        dkr[32 * dt + lq] = (G)(st.dka[dt][i] * p.scale);
+        dvr[32 * dt + lq] = (G)st.dva[dt][i];
       }
     }
   }
@@ -762,7 +763,7 @@ __device__ __forceinline__ void dkdv_half(DkvAcc<D>& st, const char* Qh, const c
 
 // Wave w takes keys kb + 32 (w % 4) .. +31 and the query half w / 4 of every
 // block; the two waves of a key slice add their partial dK, dV at the end.
-template <int D>
+template <int D, bool GB = false>
 __global__ void __launch_bounds__(kThreads8, 1) k_bwd_dkdv8(BwdParams p) {
   constexpr int TB = tile_bytes<D>();
   constexpr int NW = kThreads8 / 64;
@@ -786,14 +787,13 @@ __global__ void __launch_bounds__(kThreads8, 1) k_bwd_dkdv8(BwdParams p) {
   const int ks = w & 3, qh = w >> 2;
   const uint32_t item = blockIdx.x / (uint32_t)p.hkv, kvh = blockIdx.x % (uint32_t)p.hkv;
   // item < cap (the grid is cap work-groups per head), so the entry is read
-  // together with the count and used only once the count admits it, and
-  // clamped to the token range (tile_item).
+  // together with the count and used only once the count admits it; every
+  // entry below the count is written, with segment bounds clamped to [0, T].
   const int4 it = *reinterpret_cast<const int4*>(p.items + 4 * item);
   if ((int32_t)item >= *p.n_items) return;
-  TileItem ti;
-  if (!tile_item(it, p.T, kBKV, ti)) return;
-  const int32_t s0 = ti.s0, L = ti.L, tile = ti.tile;
+  const int32_t s0 = it.x, L = it.y, tile = it.z;
   const int32_t kb = tile * kBKV;
+  if (kb >= L) return;
   const int32_t wk_lo = kb + 32 * ks;
   const int32_t key = wk_lo + lq;  // this lane's key (S layout: lane <-> key)
   const int32_t nqb = (L - kb + kBMk - 1) / kBMk;
@@ -888,13 +888,14 @@ __global__ void __launch_bounds__(kThreads8, 1) k_bwd_dkdv8(BwdParams p) {
     for (int i = 0; i < 16; ++i) {
       const int32_t kr = wk_lo + 8 * (i >> 2) + 4 * h + (i & 3);
       if (kr < L) {
-        const int64_t row = ((int64_t)(s0 + kr) * p.hkv + kvh) * D;
-        if (p.grad_bf16) {
+        if constexpr (GB) {
+          bf16* r = static_cast<bf16*>(outp) + ((int64_t)(s0 + kr) * p.hkv + kvh) * D;
 #pragma unroll
-          for (int dt = 0; dt < DT; ++dt) static_cast<bf16*>(outp)[row + 32 * dt + lq] = (bf16)(x[dt][i] * mul);
+          for (int dt = 0; dt < DT; ++dt) r[32 * dt + lq] = (bf16)(x[dt][i] * mul);
         } else {
+          float* r = static_cast<float*>(outp) + ((int64_t)(s0 + kr) * p.hkv + kvh) * D;
 #pragma unroll
-          for (int dt = 0; dt < DT; ++dt) static_cast<float*>(outp)[row + 32 * dt + lq] = x[dt][i] * mul;
+          for (int dt = 0; dt < DT; ++dt) r[32 * dt + lq] = x[dt][i] * mul;
         }
       }
     }
@@ -921,6 +922,34 @@ size_t attn_bwd_workspace_bytes(int dtype, const AttnDims& d) {
   if (dtype != 1) return vec_bytes(d);
   return 2 * vec_bytes(d) + schedule_bytes(d.T, d.n_seg, d.max_seqlen, kBQ / dq_heads_per_wg(d), kBNq) +
          schedule_bytes(d.T, d.n_seg, d.max_seqlen, kBKV, kBMk);
+}
+
+template <bool GB>
+static void launch_dq(int hd, int hp, unsigned grid, const BwdParams& p, hipStream_t stream) {
+  if (hd == 128) {
+    if (hp == 4) k_bwd_dq<128, 4, 128, GB><<<grid, kThreads, 0, stream>>>(p);
+    else if (hp == 2) k_bwd_dq<128, 2, 128, GB><<<grid, kThreads, 0, stream>>>(p);
+    else k_bwd_dq<128, 1, 128, GB><<<grid, kThreads, 0, stream>>>(p);
+  } else if (hd == 64) {
+    if (hp == 4) k_bwd_dq<64, 4, 64, GB><<<grid, kThreads, 0, stream>>>(p);
+    else if (hp == 2) k_bwd_dq<64, 2, 64, GB><<<grid, kThreads, 0, stream>>>(p);
+    else k_bwd_dq<64, 1, 64, GB><<<grid, kThreads, 0, stream>>>(p);
+  } else {
+    // head_dim 32: the D = 64 kernel on half-width heads
+    if (hp == 4) k_bwd_dq<64, 4, 32, GB><<<grid, kThreads, 0, stream>>>(p);
+    else if (hp == 2) k_bwd_dq<64, 2, 32, GB><<<grid, kThreads, 0, stream>>>(p);
+    else k_bwd_dq<64, 1, 32, GB><<<grid, kThreads, 0, stream>>>(p);
+  }
+}
+
+template <bool GB>
+static void launch_dkdv(int hd, unsigned grid, const BwdParams& p, hipStream_t stream) {
+  if (hd == 128)
+    k_bwd_dkdv8<128, GB><<<grid, kThreads8, 0, stream>>>(p);
+  else if (hd == 64)
+    k_bwd_dkdv<64, 64, GB><<<grid, kThreads, 0, stream>>>(p);
+  else
+    k_bwd_dkdv<64, 32, GB><<<grid, kThreads, 0, stream>>>(p);
 }
 
 hipError_t launch_attn_bwd_bf16(const AttnBwdArgs& a, hipStream_t stream) {
@@ -970,20 +999,10 @@ hipError_t launch_attn_bwd_bf16(const AttnBwdArgs& a, hipStream_t stream) {
   const unsigned grid_q = (unsigned)(sq.cap * (d.hq / hp));
   {
     ScopedKernelTimer timed(kTimeBwdDq, stream);
-    if (d.d == 128) {
-      if (hp == 4) k_bwd_dq<128, 4><<<grid_q, kThreads, 0, stream>>>(p);
-      else if (hp == 2) k_bwd_dq<128, 2><<<grid_q, kThreads, 0, stream>>>(p);
-      else k_bwd_dq<128, 1><<<grid_q, kThreads, 0, stream>>>(p);
-    } else if (d.d == 64) {
-      if (hp == 4) k_bwd_dq<64, 4><<<grid_q, kThreads, 0, stream>>>(p);
-      else if (hp == 2) k_bwd_dq<64, 2><<<grid_q, kThreads, 0, stream>>>(p);
-      else k_bwd_dq<64, 1><<<grid_q, kThreads, 0, stream>>>(p);
-    } else {
-      // head_dim 32: the D = 64 kernel on half-width heads
-      if (hp == 4) k_bwd_dq<64, 4, 32><<<grid_q, kThreads, 0, stream>>>(p);
-      else if (hp == 2) k_bwd_dq<64, 2, 32><<<grid_q, kThreads, 0, stream>>>(p);
-      else k_bwd_dq<64, 1, 32><<<grid_q, kThreads, 0, stream>>>(p);
-    }
+    if (p.grad_bf16)
+      launch_dq<true>(d.d, hp, grid_q, p, stream);
+    else
+      launch_dq<false>(d.d, hp, grid_q, p, stream);
   }
 
   e = launch_schedule(a.cu, d.n_seg, (int32_t)d.T, kBKV, kBMk, true, sk, stream);
@@ -993,12 +1012,10 @@ hipError_t launch_attn_bwd_bf16(const AttnBwdArgs& a, hipStream_t stream) {
   const unsigned grid_kv = (unsigned)(sk.cap * d.hkv);
   {
     ScopedKernelTimer timed(kTimeBwdDkdv, stream);
-    if (d.d == 128)
-      k_bwd_dkdv8<128><<<grid_kv, kThreads8, 0, stream>>>(p);
-    else if (d.d == 64)
-      k_bwd_dkdv<64><<<grid_kv, kThreads, 0, stream>>>(p);
+    if (p.grad_bf16)
+      launch_dkdv<true>(d.d, grid_kv, p, stream);
     else
-      k_bwd_dkdv<64, 32><<<grid_kv, kThreads, 0, stream>>>(p);
+      launch_dkdv<false>(d.d, grid_kv, p, stream);
   }
   return hipGetLastError();
 }

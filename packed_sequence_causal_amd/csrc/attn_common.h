@@ -165,7 +165,8 @@ __device__ __forceinline__ void load_tile_async(const bf16* base, int64_t stride
     const int tu = wu + NW * i;
     const int g = t >> 3;
     const int r = 8 * (t & 7) + rr;
-    const int c = (8 * g + (p ^ lds_swz(r))) % (DR / 8);
+    const int c0 = 8 * g + (p ^ lds_swz(r));
+    const int c = DR == D ? c0 : c0 % (DR / 8);
     const bf16* src = base + (int64_t)min(row0 + r, L - 1) * stride + c * 8;
     lds_dma16(src, lds0 + (tu >> 3) * kGroupBytes + (tu & 7) * 1024);
   }
@@ -184,7 +185,8 @@ __device__ __forceinline__ void tile_offsets(int64_t stride, int w, int l, uint3
     const int t = w + NW * i;
     const int g = t >> 3;
     const int r = 8 * (t & 7) + rr;
-    const int c = (8 * g + (p ^ lds_swz(r))) % (DR / 8);
+    const int c0 = 8 * g + (p ^ lds_swz(r));
+    const int c = DR == D ? c0 : c0 % (DR / 8);
     off[i] = (uint32_t)(((int64_t)r * stride + c * 8) * 2);
   }
 }
@@ -219,22 +221,6 @@ __device__ __forceinline__ void load_tile(const bf16* base, int64_t stride, int3
 __device__ __forceinline__ void load_vec64_async(const float* vec, int32_t row0, int32_t L, void* lds, int l) {
   const int32_t row = min(row0 + l, L - 1);
   lds_dma4(vec + row, lds_addr(lds));
-}
-
-// A schedule entry (segment start, segment length, tile index) clamped to the
-// token range [0, T).  The list is built on the device from cu_seqlens, and a
-// cu_seqlens that breaks its precondition can leave slots unwritten; clamped,
-// no entry can address outside the tensors.  Returns false when the tile lies
-// past its segment (nothing to do).
-struct TileItem {
-  int32_t s0, L, tile;
-};
-__device__ __forceinline__ bool tile_item(const int4& it, int64_t T, int rows, TileItem& out) {
-  const int32_t t = (int32_t)T;
-  out.s0 = min(max(it.x, 0), t);
-  out.L = min(max(it.y, 0), t - out.s0);
-  out.tile = it.z;
-  return it.z >= 0 && out.L > 0 && it.z <= (out.L - 1) / rows;
 }
 
 // Scheduling hints: keep `n` LDS reads / MFMAs / VALU ops together, in the

@@ -147,15 +147,15 @@ __global__ void __launch_bounds__(kThreads, 2) k_attn_fwd(FwdParams p) {
   const int hw = w % HP, rs = w / HP;
   const int32_t head = (int32_t)hg * HP + hw;
   // item < cap (the grid is cap work-groups per head), so the entry is read
-  // together with the count and used only once the count admits it, and
-  // clamped to the token range (tile_item): a malformed cu_seqlens cannot
-  // send any access outside the tensors.
+  // together with the count and used only once the count admits it.  The
+  // schedule writes every entry below the count, with segment bounds clamped
+  // to [0, T]: a malformed cu_seqlens cannot send any access outside the
+  // tensors.
   const int4 it = *reinterpret_cast<const int4*>(p.items + 4 * item);
   if ((int32_t)item >= *p.n_items) return;
-  TileItem ti;
-  if (!tile_item(it, p.T, RW, ti)) return;
-  const int32_t s0 = ti.s0, L = ti.L, tile = ti.tile;
+  const int32_t s0 = it.x, L = it.y, tile = it.z;
   const int32_t q0 = tile * RW;
+  if (q0 >= L) return;
   const int32_t kvh = (int32_t)hg * HP / p.group;
 
   const bf16* Qp = p.q + (int64_t)s0 * p.sq + (int64_t)head * DR;

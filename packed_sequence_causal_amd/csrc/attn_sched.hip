@@ -33,10 +33,13 @@ __device__ inline int32_t seg_len(const int32_t* cu, int32_t s, int32_t T) {
 }
 
 // One block: zero the histogram, count each segment's tiles and scan them
-// into toff[0..n_seg] (toff[n_seg] = number of tiles).  n_items gets that
-// count clamped to the list's capacity: only a cu_seqlens that breaks its
-// precondition can exceed it, and consumers must never read past the entries
-// k_sched_fill wrote.
+// into toff[0..n_seg] (toff[n_seg] = number of tiles), and publish the count
+// in n_items.  A count above the list's capacity (only a cu_seqlens that
+// breaks its precondition gives one: clamped segments of a valid one hold at
+// most T / tile + n_seg tiles) publishes 0 instead, because then some slots
+// below the capacity could stay unwritten; with a count within capacity every
+// slot below it is written (the slots of each bin, or each document's run,
+// partition [0, count)).
 __global__ void __launch_bounds__(kThreads) k_sched_tiles(const int32_t* cu, int32_t n_seg, int32_t T, int32_t tile,
                                                           int32_t* toff, int32_t* hist, int32_t n_bins,
                                                           int32_t* n_items, int64_t cap) {
@@ -67,7 +70,7 @@ __global__ void __launch_bounds__(kThreads) k_sched_tiles(const int32_t* cu, int
   }
   if (threadIdx.x == 0) {
     toff[n_seg] = carry;
-    *n_items = (int32_t)min((int64_t)carry, cap);
+    *n_items = (int64_t)carry <= cap ? carry : 0;
   }
 }
 
@@ -206,7 +209,9 @@ __global__ void __launch_bounds__(kSmallThreads) k_sched_small(const int32_t* cu
   }
   if (threadIdx.x == 0) toff[n_seg] = carry;
   __syncthreads();
-  const int32_t n = (int32_t)min((int64_t)carry, cap);
+  // beyond the capacity (a cu_seqlens that breaks its precondition) nothing
+  // is listed: part of the slots could otherwise stay unwritten
+  const int32_t n = (int64_t)carry <= cap ? carry : 0;
   if (suffix) {
     // longest tile first: histogram of tile work
     for (int32_t i = threadIdx.x; i < n; i += kSmallThreads) {
