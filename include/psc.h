@@ -257,6 +257,29 @@ int psc_varlen_attn_fwd(int dtype, const void* q, const void* k, const void* v,
                         void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * psc_varlen_attn_fwd_noalloc — psc_varlen_attn_fwd for callers that cannot
+ * allocate device memory or pass a workspace: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation.  Same arguments,
+ * results (bit for bit) and errors as psc_varlen_attn_fwd, minus the
+ * workspace: the tile schedule goes to a 4 MiB scratch array built into the
+ * library, one per GPU, held from its first use until the process ends.  The
+ * caller still owns out and lse.  No hipMalloc, hipFree or allocating call is
+ * made.  The first call on a device looks the array's address up
+ * (hipGetSymbolAddress); later calls only launch.  Calls that overlap in time
+ * on one GPU share the array and race: serialise them (one stream, or events).
+ * Returns PSC_ERR_WORKSPACE, before any HIP call, when the workspace that
+ * psc_varlen_attn_workspace reports for these sizes exceeds 4 MiB (the tile
+ * list takes 16 bytes per query tile of 32 to 128 rows and about 20 bytes per
+ * segment: millions of tokens).
+ */
+int psc_varlen_attn_fwd_noalloc(int dtype, const void* q, const void* k, const void* v,
+                                int64_t q_tok_stride, int64_t k_tok_stride, int64_t v_tok_stride,
+                                const int32_t* cu_seqlens, int32_t n_segments, int32_t max_seqlen,
+                                int64_t total_tokens, int32_t hq, int32_t hkv, int32_t head_dim,
+                                float softmax_scale, void* out, int64_t out_tok_stride, float* lse,
+                                void* stream);
+
+/*
  * psc_varlen_attn_bwd — gradients of sum(dout * out) for the forward above.
  *   out, lse: the forward's outputs for the same inputs.
  *   The workspace also carries -D_i (D_i = <dout_i, out_i>) and -lse_i / scale

@@ -9,6 +9,7 @@ Entry points (same names as the C ABI without the ``psc_`` prefix):
   pack_sizes, pack_build                  build_pack / build_unpack on the GPU
   varlen_attn_workspace, varlen_attn_fwd, varlen_attn_bwd
                                           document-causal attention (bf16 or fp32)
+  varlen_attn_fwd_noalloc                 the forward with the library's own scratch
   check_cu_seqlens, cu_seqlens_status     device check of the cu_seqlens precondition
   rope                                    rotary embedding at the packer's indexes
   row_max_seqlen, unpack_data, split_sequence
@@ -60,6 +61,10 @@ _SIGNATURES = {
                                            ctypes.c_int64, _vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
                                            ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_float, _vp,
                                            ctypes.c_int64, _vp, _vp, ctypes.c_size_t, _vp]),
+    "psc_varlen_attn_fwd_noalloc": (ctypes.c_int, [ctypes.c_int, _vp, _vp, _vp, ctypes.c_int64, ctypes.c_int64,
+                                                   ctypes.c_int64, _vp, ctypes.c_int32, ctypes.c_int32,
+                                                   ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                                   ctypes.c_float, _vp, ctypes.c_int64, _vp, _vp]),
     "psc_varlen_attn_bwd": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int64,
                                            ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, _vp,
                                            ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32,
@@ -269,6 +274,34 @@ def varlen_attn_fwd(q, k, v, cu_seqlens, max_seqlen: int, n_segments: Optional[i
                                      _tok_stride(v, "v"), _ptr(cu_seqlens), nseg, max_seqlen, T, hq, hkv, D,
                                      float(softmax_scale or 0.0), _ptr(out), _tok_stride(out, "out"), _ptr(lse),
                                      _ptr(workspace), workspace.numel(), _stream(stream)), "psc_varlen_attn_fwd")
+    return out, lse
+
+
+def varlen_attn_fwd_noalloc(q, k, v, cu_seqlens, max_seqlen: int, n_segments: Optional[int] = None,
+                            softmax_scale: Optional[float] = None, out=None, lse=None, stream=None):
+    """varlen_attn_fwd through psc_varlen_attn_fwd_noalloc: the library keeps
+    the schedule in its own per-GPU scratch, so a caller that passes out and
+    lse makes the call allocate nothing (calls overlapping on one GPU race)."""
+    import torch
+
+    T, hq, D = q.shape
+    hkv = k.shape[1]
+    dt = _dtype_code(q)
+    nseg = cu_seqlens.numel() - 1 if n_segments is None else n_segments
+    _check_inputs(q, k, v, cu_seqlens, nseg)
+    with _on(stream):
+        if out is None:
+            out = torch.empty(T, hq, D, dtype=q.dtype, device=q.device)
+        if lse is None:
+            lse = torch.empty(hq, T, dtype=torch.float32, device=q.device)
+    if out.dim() != 3 or tuple(out.shape) != (T, hq, D) or out.dtype != q.dtype or out.device != q.device:
+        raise ValueError(f"out must be a {q.dtype} [T, hq, D] = {(T, hq, D)} tensor on {q.device}")
+    _expect(lse, "lse", (hq, T), torch.float32, q.device)
+    _check(lib().psc_varlen_attn_fwd_noalloc(dt, _ptr(q), _ptr(k), _ptr(v), _tok_stride(q, "q"),
+                                             _tok_stride(k, "k"), _tok_stride(v, "v"), _ptr(cu_seqlens), nseg,
+                                             max_seqlen, T, hq, hkv, D, float(softmax_scale or 0.0), _ptr(out),
+                                             _tok_stride(out, "out"), _ptr(lse), _stream(stream)),
+           "psc_varlen_attn_fwd_noalloc")
     return out, lse
 
 

@@ -4,6 +4,7 @@
 #include <cmath>
 #include <cstdint>
 #include <limits>
+#include <mutex>
 
 #include "../../include/psc.h"
 #include "psc_internal.h"
@@ -91,6 +92,88 @@ int debug_check_cu(const int32_t* cu, int32_t n_seg, int64_t T, void* ws, size_t
 }
 #endif
 
+// Argument checks of the forward (both entry points), host only.
+int fwd_checks(int dtype, const void* q, const void* k, const void* v, int64_t q_tok_stride, int64_t k_tok_stride,
+               int64_t v_tok_stride, const int32_t* cu_seqlens, int32_t n_segments, int32_t max_seqlen,
+               int64_t total_tokens, int32_t hq, int32_t hkv, int32_t head_dim, float softmax_scale,
+               const void* out, int64_t out_tok_stride, const float* lse, psc::AttnDims* d) {
+  int st = attn_dims(dtype, total_tokens, n_segments, max_seqlen, hq, hkv, head_dim, softmax_scale, d);
+  if (st != PSC_OK) return st;
+  const int64_t T = total_tokens;
+  if (!operand_ok(q, q_tok_stride, hq, head_dim, dtype, T) || !operand_ok(k, k_tok_stride, hkv, head_dim, dtype, T) ||
+      !operand_ok(v, v_tok_stride, hkv, head_dim, dtype, T) ||
+      !operand_ok(out, out_tok_stride, hq, head_dim, dtype, T))
+    return PSC_ERR_INVALID;
+  if (T > 0 && (!cu_seqlens || !lse)) return PSC_ERR_INVALID;
+  return PSC_OK;
+}
+
+// Launch of a checked forward with a workspace of at least `need` bytes.
+int fwd_launch(int dtype, const psc::AttnDims& d, const void* q, const void* k, const void* v, int64_t sq, int64_t sk,
+               int64_t sv, const int32_t* cu_seqlens, void* out, int64_t so, float* lse, void* workspace, size_t need,
+               hipStream_t stream) {
+#ifdef PSC_DEBUG_CHECKS
+  if (int c = debug_check_cu(cu_seqlens, d.n_seg, d.T, workspace, need, stream)) return c;
+#else
+  (void)need;
+#endif
+  psc::AttnFwdArgs a;
+  a.dims = d;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.sq = sq;
+  a.sk = sk;
+  a.sv = sv;
+  a.so = so;
+  a.cu = cu_seqlens;
+  a.out = out;
+  a.lse = lse;
+  a.workspace = workspace;
+  hipError_t e = dtype == PSC_BF16 ? psc::launch_attn_fwd_bf16(a, stream) : psc::launch_attn_fwd_f32(a, stream);
+  return e == hipSuccess ? PSC_OK : PSC_ERR_HIP;
+}
+
+// ------------------------------------------------- allocation-free forward
+//
+// psc_varlen_attn_fwd_noalloc keeps its workspace (the tile schedule) in this
+// file-scope device array instead of a caller buffer.  Each GPU the library
+// runs on holds its own copy, at its own address, until the process ends.  On
+// the host `scratch` names a host-side stand-in, never the device memory: its
+// device address is looked up once per device with hipGetSymbolAddress (with
+// that device current) and only that address is passed to kernels.  Nothing in
+// it has to start at zero: the schedule kernel clears its own histogram and
+// writes every entry the attention kernel reads.  All calls on one GPU share
+// the array, so calls that overlap in time on one GPU race.
+constexpr size_t kScratchBytes = size_t(4) << 20;
+static __device__ __attribute__((aligned(256))) char scratch[kScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the device that runs `stream`.
+int scratch_for(hipStream_t stream, void** out) {
+  int dev = 0, cur = 0;
+  if (hipGetDevice(&cur) != hipSuccess) return PSC_ERR_HIP;
+  if (stream) {
+    if (hipStreamGetDevice(stream, &dev) != hipSuccess) return PSC_ERR_HIP;
+  } else {
+    dev = cur;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return PSC_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    if (dev != cur && hipSetDevice(dev) != hipSuccess) return PSC_ERR_HIP;
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (dev != cur) (void)hipSetDevice(cur);
+    if (e != hipSuccess || !ptr) return PSC_ERR_HIP;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return PSC_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -176,38 +259,36 @@ int psc_varlen_attn_fwd(int dtype, const void* q, const void* k, const void* v, 
                         float softmax_scale, void* out, int64_t out_tok_stride, float* lse, void* workspace,
                         size_t workspace_bytes, void* stream) {
   psc::AttnDims d;
-  int st = attn_dims(dtype, total_tokens, n_segments, max_seqlen, hq, hkv, head_dim, softmax_scale, &d);
+  int st = fwd_checks(dtype, q, k, v, q_tok_stride, k_tok_stride, v_tok_stride, cu_seqlens, n_segments, max_seqlen,
+                      total_tokens, hq, hkv, head_dim, softmax_scale, out, out_tok_stride, lse, &d);
   if (st != PSC_OK) return st;
   const int64_t T = total_tokens;
-  if (!operand_ok(q, q_tok_stride, hq, head_dim, dtype, T) || !operand_ok(k, k_tok_stride, hkv, head_dim, dtype, T) ||
-      !operand_ok(v, v_tok_stride, hkv, head_dim, dtype, T) ||
-      !operand_ok(out, out_tok_stride, hq, head_dim, dtype, T))
-    return PSC_ERR_INVALID;
-  if (T > 0 && (!cu_seqlens || !lse)) return PSC_ERR_INVALID;
   const size_t need = workspace_for(0, dtype, d);
   if (T > 0 && (!workspace || workspace_bytes < need)) return PSC_ERR_WORKSPACE;
   if (T == 0) return PSC_OK;
-#ifdef PSC_DEBUG_CHECKS
-  if (int c = debug_check_cu(cu_seqlens, n_segments, T, workspace, need, static_cast<hipStream_t>(stream)))
-    return c;
-#endif
+  return fwd_launch(dtype, d, q, k, v, q_tok_stride, k_tok_stride, v_tok_stride, cu_seqlens, out, out_tok_stride,
+                    lse, workspace, need, static_cast<hipStream_t>(stream));
+}
 
-  psc::AttnFwdArgs a;
-  a.dims = d;
-  a.q = q;
-  a.k = k;
-  a.v = v;
-  a.sq = q_tok_stride;
-  a.sk = k_tok_stride;
-  a.sv = v_tok_stride;
-  a.so = out_tok_stride;
-  a.cu = cu_seqlens;
-  a.out = out;
-  a.lse = lse;
-  a.workspace = workspace;
+int psc_varlen_attn_fwd_noalloc(int dtype, const void* q, const void* k, const void* v, int64_t q_tok_stride,
+                                int64_t k_tok_stride, int64_t v_tok_stride, const int32_t* cu_seqlens,
+                                int32_t n_segments, int32_t max_seqlen, int64_t total_tokens, int32_t hq,
+                                int32_t hkv, int32_t head_dim, float softmax_scale, void* out,
+                                int64_t out_tok_stride, float* lse, void* stream) {
+  psc::AttnDims d;
+  int st = fwd_checks(dtype, q, k, v, q_tok_stride, k_tok_stride, v_tok_stride, cu_seqlens, n_segments, max_seqlen,
+                      total_tokens, hq, hkv, head_dim, softmax_scale, out, out_tok_stride, lse, &d);
+  if (st != PSC_OK) return st;
+  const int64_t T = total_tokens;
+  const size_t need = workspace_for(0, dtype, d);
+  if (need > kScratchBytes) return PSC_ERR_WORKSPACE;  // beyond the built-in scratch
+  if (T == 0) return PSC_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = dtype == PSC_BF16 ? psc::launch_attn_fwd_bf16(a, s) : psc::launch_attn_fwd_f32(a, s);
-  return e == hipSuccess ? PSC_OK : PSC_ERR_HIP;
+  void* ws = nullptr;
+  st = scratch_for(s, &ws);
+  if (st != PSC_OK) return st;
+  return fwd_launch(dtype, d, q, k, v, q_tok_stride, k_tok_stride, v_tok_stride, cu_seqlens, out, out_tok_stride,
+                    lse, ws, need, s);
 }
 
 int psc_varlen_attn_bwd(int dtype, int grad_dtype, const void* q, const void* k, const void* v, const void* out,

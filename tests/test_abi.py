@@ -301,3 +301,18 @@ def test_split_and_row_max_no_ops():
     assert L.psc_row_max_seqlen(None, 0, None, 0, None, None) == psc.ERR_INVALID
     assert L.psc_row_max_seqlen(_vp(16), 4, _vp(16), 2, None, None) == psc.ERR_INVALID
     assert L.psc_row_max_seqlen(_vp(16), 4, _vp(16), -1, _vp(16), None) == psc.ERR_INVALID
+
+
+def test_noalloc_forward_rejects_sizes_beyond_its_scratch():
+    # 2^28 tokens need a 128 MiB tile list, beyond the 4 MiB built-in scratch:
+    # rejected before any HIP call (the fake pointers are never used)
+    T = 1 << 28
+    v = ctypes.c_void_p(256)
+    L = psc.lib()
+    assert L.psc_varlen_attn_fwd_noalloc(psc.BF16, v, v, v, 1024, 256, 256, v, 1, T, T, 8, 2, 128, 0.0, v, 1024, v,
+                                         None) == psc.ERR_WORKSPACE
+    # argument checks come first, as in psc_varlen_attn_fwd
+    assert L.psc_varlen_attn_fwd_noalloc(psc.BF16, None, v, v, 1024, 256, 256, v, 1, 16, 16, 8, 2, 128, 0.0, v,
+                                         1024, v, None) == psc.ERR_INVALID
+    assert L.psc_varlen_attn_fwd_noalloc(psc.BF16, v, v, v, 1024, 256, 256, v, 1, 16, 16, 8, 2, 96, 0.0, v, 1024,
+                                         v, None) == psc.ERR_UNSUPPORTED
