@@ -210,6 +210,71 @@ def rope_rate(psc, torch, np, qd, kd, pk, w, args):
             "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "launches": launches}
 
 
+def rope_step_rate(psc, torch, np, ctx, w, steps):
+    """The step with the rotary embedding of q and k at the packer's indexes,
+    two ways, same inputs, timed by events around each whole step:
+      separate: psc_rope on q, k; attention fwd and bwd on the rotated q, k;
+                psc_rope's inverse on the fp32 dq, dk (gradients of the
+                unrotated q, k);
+      fused:    psc_varlen_attn_fwd_rope (k turned by the rotation kernel, q
+                inside the forward) and psc_varlen_attn_bwd_rope (dq, dk turned
+                back in the dQ and dK kernels' epilogues).
+    Results are bit-identical (tests/test_gpu_rope_fused.py)."""
+    a = w.attn
+    qd, kd = ctx["qd"], ctx["kd"]
+    T, hq, D = qd.shape
+    if not a.backward or a.dtype != "bf16" or D not in (64, 128):
+        return None
+    pos = ctx["pk"]["indexes"][: w.pack.keep_rows].reshape(-1)[:T].contiguous()
+    if pos.numel() != T:
+        return None
+    cu, ml, nseg = ctx["cu"], ctx["max_seqlen"], ctx["n_seg"]
+    vd, dod = ctx["vd"], ctx["dod"]
+    q2, k2 = qd.clone(), kd.clone()
+    o = torch.empty_like(qd)
+    lse = torch.empty(hq, T, dtype=torch.float32, device=qd.device)
+    f32 = dict(dtype=torch.float32, device=qd.device)
+    g = (torch.empty(T, hq, D, **f32), torch.empty(T, kd.shape[1], D, **f32), torch.empty(T, kd.shape[1], D, **f32))
+    dt = psc.BF16
+
+    def sizes(pass_):
+        return torch.empty(psc.varlen_attn_workspace(pass_, dt, T, nseg, ml, hq, kd.shape[1], D), dtype=torch.uint8,
+                           device=qd.device)
+
+    wf, wb, wfr, wbr = sizes(0), sizes(1), sizes(2), sizes(3)
+
+    def sep():
+        psc.rope(q2, k2, pos)
+        psc.varlen_attn_fwd(q2, k2, vd, cu, ml, n_segments=nseg, out=o, lse=lse, workspace=wf)
+        psc.varlen_attn_bwd(q2, k2, vd, o, dod, lse, cu, ml, n_segments=nseg, dq=g[0], dk=g[1], dv=g[2],
+                            workspace=wb)
+        psc.rope(g[0], g[1], pos, inverse=True)
+
+    def fus():
+        psc.varlen_attn_fwd_rope(q2, k2, vd, cu, ml, pos, n_segments=nseg, out=o, lse=lse, workspace=wfr)
+        psc.varlen_attn_bwd_rope(q2, k2, vd, o, dod, lse, cu, ml, pos, n_segments=nseg, dq=g[0], dk=g[1], dv=g[2],
+                                 workspace=wbr)
+
+    res = {}
+    for rnd in range(2):  # alternate the two, twice, and keep the second round
+        for name, fn in (("separate", sep), ("fused", fus)):
+            q2.copy_(qd)
+            k2.copy_(kd)
+            for _ in range(2):
+                fn()
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+            torch.cuda.synchronize()
+            ev[0].record()
+            for i in range(steps):
+                fn()
+                ev[i + 1].record()
+            torch.cuda.synchronize()
+            res[name] = float(np.median([ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]))
+    return {"separate_ms": round(res["separate"], 4), "fused_ms": round(res["fused"], 4),
+            "saving_ms": round(res["separate"] - res["fused"], 4), "steps": steps,
+            "what": "rope(q,k)+fwd+bwd+rope^-1(dq,dk) vs fwd_rope+bwd_rope, fp32 gradients"}
+
+
 def data_steps_rate(psc, torch, np, pk, w):
     """The data steps after the packer on this workload's packer output, timed
     apart from the step: per-row max_seqlen, unpack_data with the workload's
@@ -407,8 +472,9 @@ def measure(w, args, steps, warmup, torch, np, psc):
         summary["bwd"] = {"ms": round(bwd_ms, 4), "min_ms": round(float(min(bwd_all)), 4),
                           "tflops": round(bwd_flops / (bwd_ms * 1e-3) / 1e12, 2),
                           "pct_peak": round(100 * bwd_flops / (bwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2)}
-    ctx = dict(q=q, k=k, v=v, do=do, qd=qd, kd=kd, pk=pk, cu_h=cu_h, real=real, kt=kt, ms=ms, value=value,
-               fwd_flops=fwd_flops, bwd_flops=bwd_flops)
+    ctx = dict(q=q, k=k, v=v, do=do, qd=qd, kd=kd, vd=vd, dod=dod, pk=pk, cu=cu, cu_h=cu_h, n_seg=n_seg,
+               max_seqlen=max_seqlen, real=real, kt=kt, ms=ms, value=value, fwd_flops=fwd_flops,
+               bwd_flops=bwd_flops)
     return summary, ctx
 
 
@@ -480,6 +546,7 @@ def main():
     if a.backward:
         result["bwd"] = summ["bwd"]
     result["rope"] = rope_rate(psc, torch, np, ctx["qd"], ctx["kd"], ctx["pk"], w, args)
+    result["rope_step"] = rope_step_rate(psc, torch, np, ctx, w, min(args.steps, 10))
     result["data_steps"] = data_steps_rate(psc, torch, np, ctx["pk"], w)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, ctx["q"], ctx["k"], ctx["v"], ctx["do"], ctx["cu_h"], ctx["real"],

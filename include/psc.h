@@ -236,7 +236,9 @@ int psc_rope(int dtype, void* q, int64_t q_tok_stride, int32_t hq, void* k, int6
  * outside the triangles is visited (section 5.1).
  */
 
-/* psc_varlen_attn_workspace — scratch bytes for pass 0 (fwd) or 1 (bwd). */
+/* psc_varlen_attn_workspace — scratch bytes for pass 0 (psc_varlen_attn_fwd),
+ * 1 (psc_varlen_attn_bwd), 2 (psc_varlen_attn_fwd_rope) or 3
+ * (psc_varlen_attn_bwd_rope). */
 int psc_varlen_attn_workspace(int pass, int dtype, int64_t total_tokens, int32_t n_segments,
                               int32_t max_seqlen, int32_t hq, int32_t hkv, int32_t head_dim,
                               size_t* bytes /* host out */);
@@ -301,6 +303,52 @@ int psc_varlen_attn_bwd(int dtype, int grad_dtype, const void* q, const void* k,
                         int64_t total_tokens, int32_t hq, int32_t hkv, int32_t head_dim,
                         float softmax_scale, void* dq, void* dk, void* dv,
                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Rotary embedding fused with the attention (bf16, head_dim 64 or 128).
+ *
+ * The model rotates q and k by each token's position inside its segment before
+ * attention (InternEvo "数据加载与流程", section "获取Dataloader数据": the
+ * packer's indexes; XTuner sequence-parallel page, section "实现方案": the
+ * rotation right before attention), and its backward turns dq and dk back.
+ * The turn is the one psc_rope applies (rotate-half pairs i, i + D/2 by
+ * positions[t] * base^(-2i/D); same angles and arithmetic, so the results are
+ * those of psc_rope followed by the plain attention calls, bit for bit).
+ * positions: int32 [T], 0 <= positions[t] < max_seqlen (true of the packer's
+ * indexes; other values are clamped into that range, never out of bounds).
+ *
+ * psc_varlen_attn_fwd_rope — attention of the rotated q and k.  q and k are
+ *   rotated IN PLACE (on return they hold the rotated q~, k~ that the backward
+ *   takes): k by the rotation kernel, q inside the attention kernel as each
+ *   row is loaded (then written back).  Other arguments as
+ *   psc_varlen_attn_fwd; workspace from psc_varlen_attn_workspace(2, ...)
+ *   (it also holds the step's cos/sin table).
+ * psc_varlen_attn_bwd_rope — gradients with respect to the UNROTATED q, k
+ *   (and v) from the rotated q~, k~ the forward left: the dQ and dK kernels
+ *   turn their results back by -theta before storing them, so no separate
+ *   rotation pass over the gradients is needed.  Other arguments as
+ *   psc_varlen_attn_bwd; workspace from psc_varlen_attn_workspace(3, ...).
+ * Errors: as the plain calls, plus PSC_ERR_UNSUPPORTED for fp32 inputs or a
+ * head_dim other than 64 and 128, PSC_ERR_INVALID for a null positions or a
+ * rope_base that is not positive and finite.
+ */
+int psc_varlen_attn_fwd_rope(int dtype, void* q, void* k, const void* v,
+                             int64_t q_tok_stride, int64_t k_tok_stride, int64_t v_tok_stride,
+                             const int32_t* cu_seqlens, int32_t n_segments, int32_t max_seqlen,
+                             int64_t total_tokens, int32_t hq, int32_t hkv, int32_t head_dim,
+                             const int32_t* positions, float rope_base, float softmax_scale,
+                             void* out, int64_t out_tok_stride, float* lse,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+int psc_varlen_attn_bwd_rope(int dtype, int grad_dtype, const void* q_rot, const void* k_rot,
+                             const void* v, const void* out, const void* dout, const float* lse,
+                             int64_t q_tok_stride, int64_t k_tok_stride, int64_t v_tok_stride,
+                             int64_t out_tok_stride, int64_t dout_tok_stride,
+                             const int32_t* cu_seqlens, int32_t n_segments, int32_t max_seqlen,
+                             int64_t total_tokens, int32_t hq, int32_t hkv, int32_t head_dim,
+                             const int32_t* positions, float rope_base, float softmax_scale,
+                             void* dq, void* dk, void* dv,
+                             void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * psc_check_cu_seqlens — device check of the cu_seqlens precondition

@@ -10,6 +10,8 @@ Entry points (same names as the C ABI without the ``psc_`` prefix):
   varlen_attn_workspace, varlen_attn_fwd, varlen_attn_bwd
                                           document-causal attention (bf16 or fp32)
   varlen_attn_fwd_noalloc                 the forward with the library's own scratch
+  varlen_attn_fwd_rope, varlen_attn_bwd_rope
+                                          attention with the rotary embedding fused in
   check_cu_seqlens, cu_seqlens_status     device check of the cu_seqlens precondition
   rope                                    rotary embedding at the packer's indexes
   row_max_seqlen, unpack_data, split_sequence
@@ -70,6 +72,15 @@ _SIGNATURES = {
                                            ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32,
                                            ctypes.c_int32, ctypes.c_int32, ctypes.c_float, _vp, _vp, _vp, _vp,
                                            ctypes.c_size_t, _vp]),
+    "psc_varlen_attn_fwd_rope": (ctypes.c_int, [ctypes.c_int, _vp, _vp, _vp, ctypes.c_int64, ctypes.c_int64,
+                                                ctypes.c_int64, _vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
+                                                ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _vp, ctypes.c_float,
+                                                ctypes.c_float, _vp, ctypes.c_int64, _vp, _vp, ctypes.c_size_t, _vp]),
+    "psc_varlen_attn_bwd_rope": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _vp,
+                                                ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                                ctypes.c_int64, _vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
+                                                ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _vp, ctypes.c_float,
+                                                ctypes.c_float, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
     "psc_check_cu_seqlens": (ctypes.c_int, [_vp, ctypes.c_int32, ctypes.c_int64, _vp, _vp]),
     "psc_cu_seqlens_status": (ctypes.c_int, [ctypes.c_int32]),
     "psc_debug_checks": (ctypes.c_int, []),
@@ -344,6 +355,89 @@ def varlen_attn_bwd(q, k, v, out, dout, lse, cu_seqlens, max_seqlen: int, n_segm
                                      max_seqlen, T, hq, hkv, D, float(softmax_scale or 0.0), _ptr(dq), _ptr(dk),
                                      _ptr(dv), _ptr(workspace), workspace.numel(), _stream(stream)),
            "psc_varlen_attn_bwd")
+    return dq, dk, dv
+
+
+def _positions(positions, T, device):
+    import torch
+
+    if positions.dtype != torch.int32 or positions.device != device or not positions.is_contiguous() \
+            or positions.numel() != T:
+        raise ValueError("positions must be a contiguous int32 tensor with one entry per token on q's device")
+
+
+def varlen_attn_fwd_rope(q, k, v, cu_seqlens, max_seqlen: int, positions, rope_base: float = 10000.0,
+                         n_segments: Optional[int] = None, softmax_scale: Optional[float] = None, out=None, lse=None,
+                         workspace=None, stream=None):
+    """Attention of q, k rotated by positions (the packer's indexes), with the
+    rotation fused in.  q and k are rotated IN PLACE (they then hold the
+    rotated q~, k~ for varlen_attn_bwd_rope).  Returns (out, lse)."""
+    import torch
+
+    T, hq, D = q.shape
+    hkv = k.shape[1]
+    dt = _dtype_code(q)
+    nseg = cu_seqlens.numel() - 1 if n_segments is None else n_segments
+    _check_inputs(q, k, v, cu_seqlens, nseg)
+    _positions(positions, T, q.device)
+    ws = varlen_attn_workspace(2, dt, T, nseg, max_seqlen, hq, hkv, D)
+    with _on(stream):
+        if out is None:
+            out = torch.empty(T, hq, D, dtype=q.dtype, device=q.device)
+        if lse is None:
+            lse = torch.empty(hq, T, dtype=torch.float32, device=q.device)
+        if workspace is None or workspace.numel() < ws:
+            workspace = torch.empty(max(ws, 256), dtype=torch.uint8, device=q.device)
+    if out.dim() != 3 or tuple(out.shape) != (T, hq, D) or out.dtype != q.dtype or out.device != q.device:
+        raise ValueError(f"out must be a {q.dtype} [T, hq, D] = {(T, hq, D)} tensor on {q.device}")
+    _expect(lse, "lse", (hq, T), torch.float32, q.device)
+    _check(lib().psc_varlen_attn_fwd_rope(dt, _ptr(q), _ptr(k), _ptr(v), _tok_stride(q, "q"), _tok_stride(k, "k"),
+                                          _tok_stride(v, "v"), _ptr(cu_seqlens), nseg, max_seqlen, T, hq, hkv, D,
+                                          _ptr(positions), float(rope_base), float(softmax_scale or 0.0), _ptr(out),
+                                          _tok_stride(out, "out"), _ptr(lse), _ptr(workspace), workspace.numel(),
+                                          _stream(stream)), "psc_varlen_attn_fwd_rope")
+    return out, lse
+
+
+def varlen_attn_bwd_rope(q_rot, k_rot, v, out, dout, lse, cu_seqlens, max_seqlen: int, positions,
+                         rope_base: float = 10000.0, n_segments: Optional[int] = None,
+                         softmax_scale: Optional[float] = None, dq=None, dk=None, dv=None, workspace=None,
+                         stream=None, grad_dtype: Optional[int] = None):
+    """Gradients with respect to the unrotated q, k (and v), from the rotated
+    q~, k~ that varlen_attn_fwd_rope left; the turn back is fused into the
+    dQ and dK kernels.  Returns (dq, dk, dv)."""
+    import torch
+
+    T, hq, D = q_rot.shape
+    hkv = k_rot.shape[1]
+    dt = _dtype_code(q_rot)
+    gdt = F32 if grad_dtype is None else grad_dtype
+    nseg = cu_seqlens.numel() - 1 if n_segments is None else n_segments
+    _check_inputs(q_rot, k_rot, v, cu_seqlens, nseg)
+    _positions(positions, T, q_rot.device)
+    for name, t in (("out", out), ("dout", dout)):
+        if t.dim() != 3 or tuple(t.shape) != (T, hq, D) or t.dtype != q_rot.dtype or t.device != q_rot.device:
+            raise ValueError(f"{name} must be a {q_rot.dtype} [T, hq, D] = {(T, hq, D)} tensor on {q_rot.device}")
+    _expect(lse, "lse", (hq, T), torch.float32, q_rot.device)
+    gtype = torch.bfloat16 if gdt == BF16 else torch.float32
+    ws = varlen_attn_workspace(3, dt, T, nseg, max_seqlen, hq, hkv, D)
+    with _on(stream):
+        g = dict(dtype=gtype, device=q_rot.device)
+        dq = torch.empty(T, hq, D, **g) if dq is None else dq
+        dk = torch.empty(T, hkv, D, **g) if dk is None else dk
+        dv = torch.empty(T, hkv, D, **g) if dv is None else dv
+        if workspace is None or workspace.numel() < ws:
+            workspace = torch.empty(max(ws, 256), dtype=torch.uint8, device=q_rot.device)
+    _expect(dq, "dq", (T, hq, D), gtype, q_rot.device)
+    _expect(dk, "dk", (T, hkv, D), gtype, q_rot.device)
+    _expect(dv, "dv", (T, hkv, D), gtype, q_rot.device)
+    _check(lib().psc_varlen_attn_bwd_rope(dt, gdt, _ptr(q_rot), _ptr(k_rot), _ptr(v), _ptr(out), _ptr(dout),
+                                          _ptr(lse), _tok_stride(q_rot, "q"), _tok_stride(k_rot, "k"),
+                                          _tok_stride(v, "v"), _tok_stride(out, "out"), _tok_stride(dout, "dout"),
+                                          _ptr(cu_seqlens), nseg, max_seqlen, T, hq, hkv, D, _ptr(positions),
+                                          float(rope_base), float(softmax_scale or 0.0), _ptr(dq), _ptr(dk), _ptr(dv),
+                                          _ptr(workspace), workspace.numel(), _stream(stream)),
+           "psc_varlen_attn_bwd_rope")
     return dq, dk, dv
 
 

@@ -32,6 +32,7 @@
 
 #include "attn_common.h"
 #include "psc_internal.h"
+#include "rope_common.h"
 
 namespace psc {
 namespace {
@@ -57,7 +58,17 @@ struct BwdParams {
   int32_t hq, hkv, group;
   float scale, scale_log2;
   int32_t grad_bf16;  // launch selection only: the kernels take it as a template parameter
+  // rotary embedding (the ROPE instantiations only): q and k arrive turned,
+  // and dq, dk are turned back by -theta before they are stored
+  const int32_t* pos;     // [T] position of each token
+  const float2* rope_cs;  // [rope_n_pos][D/2] (cos, sin)
+  int32_t rope_n_pos;
 };
+
+// (cos, sin) of the turn at token t (position clamped to the table).
+__device__ __forceinline__ const float2* rope_row(const BwdParams& p, int64_t t, int half) {
+  return p.rope_cs + (int64_t)min(max(p.pos[t], 0), p.rope_n_pos - 1) * half;
+}
 
 // ---------------------------------------------------------------------- dQ
 
@@ -164,7 +175,7 @@ __device__ __forceinline__ void dq_block(DqState<D>& st, const char* Ks, const c
 // of the head's columns, and only dQ's first DR columns are stored.
 // GB: dQ stored in bf16 (else fp32); a template parameter so the fp32
 // kernel's code and registers are those of a kernel with no bf16 path.
-template <int D, int HP, int DR = D, bool GB = false>
+template <int D, int HP, int DR = D, bool GB = false, bool ROPE = false>
 __global__ void __launch_bounds__(kThreads, 2) k_bwd_dq(BwdParams p) {
   static_assert(DR == D || 2 * DR == D, "a head fills the tile or half of it");
   constexpr int RW = kBQ / HP;  // query rows per workgroup
@@ -205,6 +216,10 @@ __global__ void __launch_bounds__(kThreads, 2) k_bwd_dq(BwdParams p) {
   const int32_t qrow = q0 + 32 * rs + lq;
   const bool qvalid = qrow < L;
   DqState<D> st;
+  // the row's rotary position, fetched before the key loop so the epilogue
+  // waits on one load (the table row), not on two in a chain
+  int32_t rope_pos = 0;
+  if constexpr (ROPE) rope_pos = qvalid ? min(max(p.pos[s0 + qrow], 0), p.rope_n_pos - 1) : 0;
   {
     const bf16* Qr = p.q + (int64_t)(s0 + qrow) * p.sq + (int64_t)head * DR;
     const bf16* Dr = p.dout + (int64_t)(s0 + qrow) * p.sdo + (int64_t)head * DR;
@@ -271,6 +286,34 @@ __global__ void __launch_bounds__(kThreads, 2) k_bwd_dq(BwdParams p) {
   // time.  Inside a staged row, 16-byte chunk c sits at slot c ^ (row % kPC).
   char* const stage = (nkv & 1) ? (w < 2 ? Ks1 : Vs1) : (w < 2 ? Ks0 : Vs0);
   char* const ob = stage + (w & 1) * (tile_bytes<D>() / 2);
+  float omul = p.scale;
+  if constexpr (ROPE) {
+    // dQ of the turned q, scaled, turned back by -theta: register i of acc[dt]
+    // is dim 32 dt + 8 (i / 4) + 4 h + i % 4 of the lane's row, so dims d and
+    // d + D/2 are acc[dt] and acc[dt + D/64] of the same lane and register
+    static_assert(DR == D, "the turn pairs registers of one lane");
+    constexpr int HD = D / 64;
+    if (qvalid) {
+      const float2* cs = p.rope_cs + (int64_t)rope_pos * (D / 2);
+#pragma unroll
+      for (int dt = 0; dt < HD; ++dt) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const float4* c4 = reinterpret_cast<const float4*>(cs + 32 * dt + 8 * g + 4 * h);
+          const float4 t0 = c4[0], t1 = c4[1];
+          const float cc[4] = {t0.x, t0.z, t1.x, t1.z}, ss[4] = {t0.y, t0.w, t1.y, t1.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            float y1, y2;
+            rope_turn(st.acc[dt][4 * g + e] * p.scale, st.acc[dt + HD][4 * g + e] * p.scale, cc[e], -ss[e], y1, y2);
+            st.acc[dt][4 * g + e] = y1;
+            st.acc[dt + HD][4 * g + e] = y2;
+          }
+        }
+      }
+    }
+    omul = 1.f;
+  }
   if constexpr (GB) {
     // bf16 dQ: whole 2*D-byte rows fit half a tile at once (as the forward's O)
     constexpr int kChunks = D / 8;
@@ -281,7 +324,7 @@ __global__ void __launch_bounds__(kThreads, 2) k_bwd_dq(BwdParams p) {
       for (int g4 = 0; g4 < 4; ++g4) {
         bf16x4 o4;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) o4[e] = (bf16)(st.acc[dt][4 * g4 + e] * p.scale);
+        for (int e = 0; e < 4; ++e) o4[e] = (bf16)(st.acc[dt][4 * g4 + e] * omul);
         const int c = 4 * dt + g4;
         *reinterpret_cast<bf16x4*>(ob + lq * (2 * D) + ((c ^ (lq & (kChunks - 1))) << 4) + 8 * h) = o4;
       }
@@ -309,7 +352,7 @@ __global__ void __launch_bounds__(kThreads, 2) k_bwd_dq(BwdParams p) {
         for (int g4 = 0; g4 < 4; ++g4) {
           f32x4 v4;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) v4[e] = st.acc[dt][4 * g4 + e] * p.scale;
+          for (int e = 0; e < 4; ++e) v4[e] = st.acc[dt][4 * g4 + e] * omul;
           const int c = (32 * dt - kPW * pass) / 4 + 2 * g4 + h;
           *reinterpret_cast<f32x4*>(ob + lq * (4 * kPW) + ((c ^ (lq & (kPC - 1))) << 4)) = v4;
         }
@@ -543,7 +586,7 @@ __device__ __forceinline__ void dkdv_block_full(DkvState<D>& st, const char* Qs,
 // DR = D / 2 runs heads of DR columns: K and V are zero past DR in registers
 // (S and dP are those of the head's columns), and only the first DR columns of
 // dK and dV are stored.
-template <int D, int DR = D, bool GB = false>
+template <int D, int DR = D, bool GB = false, bool ROPE = false>
 __global__ void __launch_bounds__(kThreads, 2) k_bwd_dkdv(BwdParams p) {
   static_assert(D == 64, "k_bwd_dkdv8 handles D = 128");
   static_assert(DR == D || 2 * DR == D, "a head fills the tile or half of it");
@@ -635,6 +678,29 @@ __global__ void __launch_bounds__(kThreads, 2) k_bwd_dkdv(BwdParams p) {
   }
 
   // dka/dva C layout: key = wk_lo + 8*(i/4) + 4*h + i%4, d = 32*dt + lq
+  float kmul = p.scale;
+  if constexpr (ROPE) {
+    // dK of the turned k, scaled, turned back by -theta: dims d and d + D/2 of
+    // a key are dka[dt] and dka[dt + D/64] of the same lane and register
+    static_assert(DR == D, "the turn pairs registers of one lane");
+    constexpr int HD = D / 64;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int32_t kr = wk_lo + 8 * (i >> 2) + 4 * h + (i & 3);
+      if (kr < L) {
+        const float2* cs = rope_row(p, s0 + kr, D / 2);
+#pragma unroll
+        for (int dt = 0; dt < HD; ++dt) {
+          const float2 t = cs[32 * dt + lq];
+          float y1, y2;
+          rope_turn(st.dka[dt][i] * p.scale, st.dka[dt + HD][i] * p.scale, t.x, -t.y, y1, y2);
+          st.dka[dt][i] = y1;
+          st.dka[dt + HD][i] = y2;
+        }
+      }
+    }
+    kmul = 1.f;
+  }
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     const int32_t kr = wk_lo + 8 * (i >> 2) + 4 * h + (i & 3);
@@ -644,7 +710,7 @@ __global__ void __launch_bounds__(kThreads, 2) k_bwd_dkdv(BwdParams p) {
       G* dvr = static_cast<G*>(p.dv) + ((int64_t)(s0 + kr) * p.hkv + kvh) * DR;
 #pragma unroll
       for (int dt = 0; dt < DR / 32; ++dt) {
-        dkr[32 * dt + lq] = (G)(st.dka[dt][i] * p.scale);
+        dkr[32 * dt + lq] = (G)(st.dka[dt][i] * kmul);
         dvr[32 * dt + lq] = (G)st.dva[dt][i];
       }
     }
@@ -763,7 +829,7 @@ __device__ __forceinline__ void dkdv_half(DkvAcc<D>& st, const char* Qh, const c
 
 // Wave w takes keys kb + 32 (w % 4) .. +31 and the query half w / 4 of every
 // block; the two waves of a key slice add their partial dK, dV at the end.
-template <int D, bool GB = false>
+template <int D, bool GB = false, bool ROPE = false>
 __global__ void __launch_bounds__(kThreads8, 1) k_bwd_dkdv8(BwdParams p) {
   constexpr int TB = tile_bytes<D>();
   constexpr int NW = kThreads8 / 64;
@@ -873,7 +939,7 @@ __global__ void __launch_bounds__(kThreads8, 1) k_bwd_dkdv8(BwdParams p) {
     }
   };
   // add the partner's part and store (C layout: key = wk_lo + 8*(i/4) + 4*h + i%4, d = 32*dt + lq)
-  auto finish = [&](f32x16* x, void* outp, float mul) {
+  auto finish = [&](f32x16* x, void* outp, float mul, bool turn) {
     const f32x4* theirs = red + (2 * ks + (qh ^ 1)) * kPieces;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
@@ -883,6 +949,31 @@ __global__ void __launch_bounds__(kThreads8, 1) k_bwd_dkdv8(BwdParams p) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) x[dt][4 * g + e] += y[e];
       }
+    }
+    if constexpr (ROPE) {
+      // dK of the turned k, scaled, turned back by -theta: dims d and d + D/2
+      // of a key are x[dt] and x[dt + D/64] of the same lane and register
+      if (turn) {
+        constexpr int HD = D / 64;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int32_t kr = wk_lo + 8 * (i >> 2) + 4 * h + (i & 3);
+          if (kr < L) {
+            const float2* cs = rope_row(p, s0 + kr, D / 2);
+#pragma unroll
+            for (int dt = 0; dt < HD; ++dt) {
+              const float2 t = cs[32 * dt + lq];
+              float y1, y2;
+              rope_turn(x[dt][i] * mul, x[dt + HD][i] * mul, t.x, -t.y, y1, y2);
+              x[dt][i] = y1;
+              x[dt + HD][i] = y2;
+            }
+          }
+        }
+        mul = 1.f;
+      }
+    } else {
+      (void)turn;
     }
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -903,8 +994,8 @@ __global__ void __launch_bounds__(kThreads8, 1) k_bwd_dkdv8(BwdParams p) {
   if (qh) give(st.dka);
   else give(st.dva);
   __syncthreads();
-  if (qh) finish(st.dva, p.dv, 1.f);
-  else finish(st.dka, p.dk, p.scale);
+  if (qh) finish(st.dva, p.dv, 1.f, false);
+  else finish(st.dka, p.dk, p.scale, true);
 }
 
 }  // namespace
@@ -924,17 +1015,17 @@ size_t attn_bwd_workspace_bytes(int dtype, const AttnDims& d) {
          schedule_bytes(d.T, d.n_seg, d.max_seqlen, kBKV, kBMk);
 }
 
-template <bool GB>
+template <bool GB, bool ROPE>
 static void launch_dq(int hd, int hp, unsigned grid, const BwdParams& p, hipStream_t stream) {
   if (hd == 128) {
-    if (hp == 4) k_bwd_dq<128, 4, 128, GB><<<grid, kThreads, 0, stream>>>(p);
-    else if (hp == 2) k_bwd_dq<128, 2, 128, GB><<<grid, kThreads, 0, stream>>>(p);
-    else k_bwd_dq<128, 1, 128, GB><<<grid, kThreads, 0, stream>>>(p);
+    if (hp == 4) k_bwd_dq<128, 4, 128, GB, ROPE><<<grid, kThreads, 0, stream>>>(p);
+    else if (hp == 2) k_bwd_dq<128, 2, 128, GB, ROPE><<<grid, kThreads, 0, stream>>>(p);
+    else k_bwd_dq<128, 1, 128, GB, ROPE><<<grid, kThreads, 0, stream>>>(p);
   } else if (hd == 64) {
-    if (hp == 4) k_bwd_dq<64, 4, 64, GB><<<grid, kThreads, 0, stream>>>(p);
-    else if (hp == 2) k_bwd_dq<64, 2, 64, GB><<<grid, kThreads, 0, stream>>>(p);
-    else k_bwd_dq<64, 1, 64, GB><<<grid, kThreads, 0, stream>>>(p);
-  } else {
+    if (hp == 4) k_bwd_dq<64, 4, 64, GB, ROPE><<<grid, kThreads, 0, stream>>>(p);
+    else if (hp == 2) k_bwd_dq<64, 2, 64, GB, ROPE><<<grid, kThreads, 0, stream>>>(p);
+    else k_bwd_dq<64, 1, 64, GB, ROPE><<<grid, kThreads, 0, stream>>>(p);
+  } else if constexpr (!ROPE) {
     // head_dim 32: the D = 64 kernel on half-width heads
     if (hp == 4) k_bwd_dq<64, 4, 32, GB><<<grid, kThreads, 0, stream>>>(p);
     else if (hp == 2) k_bwd_dq<64, 2, 32, GB><<<grid, kThreads, 0, stream>>>(p);
@@ -942,13 +1033,13 @@ static void launch_dq(int hd, int hp, unsigned grid, const BwdParams& p, hipStre
   }
 }
 
-template <bool GB>
+template <bool GB, bool ROPE>
 static void launch_dkdv(int hd, unsigned grid, const BwdParams& p, hipStream_t stream) {
   if (hd == 128)
-    k_bwd_dkdv8<128, GB><<<grid, kThreads8, 0, stream>>>(p);
+    k_bwd_dkdv8<128, GB, ROPE><<<grid, kThreads8, 0, stream>>>(p);
   else if (hd == 64)
-    k_bwd_dkdv<64, 64, GB><<<grid, kThreads, 0, stream>>>(p);
-  else
+    k_bwd_dkdv<64, 64, GB, ROPE><<<grid, kThreads, 0, stream>>>(p);
+  else if constexpr (!ROPE)
     k_bwd_dkdv<64, 32, GB><<<grid, kThreads, 0, stream>>>(p);
 }
 
@@ -977,6 +1068,9 @@ hipError_t launch_attn_bwd_bf16(const AttnBwdArgs& a, hipStream_t stream) {
   p.dk = a.dk;
   p.dv = a.dv;
   p.grad_bf16 = a.grad_bf16;
+  p.pos = a.rope.pos;
+  p.rope_cs = a.rope.rope_cs;
+  p.rope_n_pos = a.rope.rope_n_pos;
   p.sq = a.sq;
   p.sk = a.sk;
   p.sv = a.sv;
@@ -999,10 +1093,13 @@ hipError_t launch_attn_bwd_bf16(const AttnBwdArgs& a, hipStream_t stream) {
   const unsigned grid_q = (unsigned)(sq.cap * (d.hq / hp));
   {
     ScopedKernelTimer timed(kTimeBwdDq, stream);
-    if (p.grad_bf16)
-      launch_dq<true>(d.d, hp, grid_q, p, stream);
-    else
-      launch_dq<false>(d.d, hp, grid_q, p, stream);
+    if (p.rope_cs) {
+      if (p.grad_bf16) launch_dq<true, true>(d.d, hp, grid_q, p, stream);
+      else launch_dq<false, true>(d.d, hp, grid_q, p, stream);
+    } else {
+      if (p.grad_bf16) launch_dq<true, false>(d.d, hp, grid_q, p, stream);
+      else launch_dq<false, false>(d.d, hp, grid_q, p, stream);
+    }
   }
 
   e = launch_schedule(a.cu, d.n_seg, (int32_t)d.T, kBKV, kBMk, true, sk, stream);
@@ -1012,10 +1109,13 @@ hipError_t launch_attn_bwd_bf16(const AttnBwdArgs& a, hipStream_t stream) {
   const unsigned grid_kv = (unsigned)(sk.cap * d.hkv);
   {
     ScopedKernelTimer timed(kTimeBwdDkdv, stream);
-    if (p.grad_bf16)
-      launch_dkdv<true>(d.d, grid_kv, p, stream);
-    else
-      launch_dkdv<false>(d.d, grid_kv, p, stream);
+    if (p.rope_cs) {
+      if (p.grad_bf16) launch_dkdv<true, true>(d.d, grid_kv, p, stream);
+      else launch_dkdv<false, true>(d.d, grid_kv, p, stream);
+    } else {
+      if (p.grad_bf16) launch_dkdv<true, false>(d.d, grid_kv, p, stream);
+      else launch_dkdv<false, false>(d.d, grid_kv, p, stream);
+    }
   }
   return hipGetLastError();
 }

@@ -29,6 +29,7 @@
 // Epilogue: O / l in bf16, lse = (m + log2 l) * ln 2 in fp32.
 #include "attn_common.h"
 #include "psc_internal.h"
+#include "rope_common.h"
 
 namespace psc {
 namespace {
@@ -48,6 +49,11 @@ struct FwdParams {
   const int32_t* n_items;
   int32_t hq, group;
   float scale_log2;
+  // rotary embedding of q inside the kernel (the ROPE instantiations only)
+  bf16* q_rot;             // q turned, written in place
+  const int32_t* pos;      // [T] position of each token
+  const float2* rope_cs;   // [rope_n_pos][D/2] (cos, sin)
+  int32_t rope_n_pos;
 };
 
 // Asynchronous loads of key/value rows [kb, kb + 64) into one LDS stage.
@@ -130,7 +136,11 @@ __device__ __forceinline__ void fwd_block(FwdState<D>& st, const char* Ks, const
 // DR are zero in registers (so the scores are those of the DR columns), the
 // tile loader repeats the head's columns there, and only O's first DR
 // columns are stored.
-template <int D, int HP, int DR = D>
+// ROPE: Q's rows are turned by their tokens' positions as they are loaded
+// (rope_common.h; K arrives already turned) and written back in place, so the
+// backward reads the turned q.  Each (row, head) of q belongs to one
+// workgroup, which reads it before writing it.
+template <int D, int HP, int DR = D, bool ROPE = false>
 __global__ void __launch_bounds__(kThreads, 2) k_attn_fwd(FwdParams p) {
   static_assert(DR == D || 2 * DR == D, "a head fills the tile or half of it");
   constexpr int RW = kBM / HP;  // query rows per workgroup
@@ -177,6 +187,34 @@ __global__ void __launch_bounds__(kThreads, 2) k_attn_fwd(FwdParams p) {
     st.qf[kk] = qvalid && 16 * kk + 8 * h < DR
                     ? *reinterpret_cast<const bf16x8*>(Qp + (int64_t)qrow * p.sq + 16 * kk + 8 * h)
                     : bf16x8{};
+  }
+  if constexpr (ROPE) {
+    // dims i and i + DR/2 of the lane's row sit in k-steps kk and kk + DR/32
+    // (element j) of the same lane
+    static_assert(DR == D, "the turn pairs k-steps of one lane");
+    constexpr int HK = DR / 32;
+    if (qvalid) {
+      const int32_t pos = min(max(p.pos[s0 + qrow], 0), p.rope_n_pos - 1);
+      const float2* cs = p.rope_cs + (int64_t)pos * (DR / 2) + 8 * h;
+#pragma unroll
+      for (int kk = 0; kk < HK; ++kk) {
+        float4 t4[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) t4[u] = reinterpret_cast<const float4*>(cs + 16 * kk)[u];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float c = (j & 1) ? t4[j >> 1].z : t4[j >> 1].x;
+          const float sn = (j & 1) ? t4[j >> 1].w : t4[j >> 1].y;
+          float y1, y2;
+          rope_turn((float)st.qf[kk][j], (float)st.qf[kk + HK][j], c, sn, y1, y2);
+          st.qf[kk][j] = (bf16)y1;
+          st.qf[kk + HK][j] = (bf16)y2;
+        }
+      }
+      bf16* Qw = p.q_rot + (int64_t)(s0 + qrow) * p.sq + (int64_t)head * DR;
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk) *reinterpret_cast<bf16x8*>(Qw + 16 * kk + 8 * h) = st.qf[kk];
+    }
   }
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) st.oacc[dt] = f32x16{};
@@ -253,6 +291,24 @@ size_t attn_fwd_workspace_bytes(int dtype, const AttnDims& d) {
   return schedule_bytes(d.T, d.n_seg, d.max_seqlen, kBM / heads_per_wg(d), kBN);
 }
 
+template <bool ROPE>
+static void launch_fwd(int hd, int hp, unsigned g, const FwdParams& p, hipStream_t stream) {
+  if (hd == 128) {
+    if (hp == 4) k_attn_fwd<128, 4, 128, ROPE><<<g, kThreads, 0, stream>>>(p);
+    else if (hp == 2) k_attn_fwd<128, 2, 128, ROPE><<<g, kThreads, 0, stream>>>(p);
+    else k_attn_fwd<128, 1, 128, ROPE><<<g, kThreads, 0, stream>>>(p);
+  } else if (hd == 64) {
+    if (hp == 4) k_attn_fwd<64, 4, 64, ROPE><<<g, kThreads, 0, stream>>>(p);
+    else if (hp == 2) k_attn_fwd<64, 2, 64, ROPE><<<g, kThreads, 0, stream>>>(p);
+    else k_attn_fwd<64, 1, 64, ROPE><<<g, kThreads, 0, stream>>>(p);
+  } else if constexpr (!ROPE) {
+    // head_dim 32: the D = 64 kernel on half-width heads (no in-kernel turn)
+    if (hp == 4) k_attn_fwd<64, 4, 32><<<g, kThreads, 0, stream>>>(p);
+    else if (hp == 2) k_attn_fwd<64, 2, 32><<<g, kThreads, 0, stream>>>(p);
+    else k_attn_fwd<64, 1, 32><<<g, kThreads, 0, stream>>>(p);
+  }
+}
+
 hipError_t launch_attn_fwd_bf16(const AttnFwdArgs& a, hipStream_t stream) {
   const AttnDims& d = a.dims;
   const int hp = heads_per_wg(d);
@@ -280,19 +336,14 @@ hipError_t launch_attn_fwd_bf16(const AttnFwdArgs& a, hipStream_t stream) {
   if (grid == 0) return hipSuccess;
   ScopedKernelTimer timed(kTimeFwd, stream);
   const unsigned g = (unsigned)(grid / hp);
-  if (d.d == 128) {
-    if (hp == 4) k_attn_fwd<128, 4><<<g, kThreads, 0, stream>>>(p);
-    else if (hp == 2) k_attn_fwd<128, 2><<<g, kThreads, 0, stream>>>(p);
-    else k_attn_fwd<128, 1><<<g, kThreads, 0, stream>>>(p);
-  } else if (d.d == 64) {
-    if (hp == 4) k_attn_fwd<64, 4><<<g, kThreads, 0, stream>>>(p);
-    else if (hp == 2) k_attn_fwd<64, 2><<<g, kThreads, 0, stream>>>(p);
-    else k_attn_fwd<64, 1><<<g, kThreads, 0, stream>>>(p);
+  if (a.rope.rope_cs) {
+    p.q_rot = static_cast<bf16*>(const_cast<void*>(a.q));
+    p.pos = a.rope.pos;
+    p.rope_cs = a.rope.rope_cs;
+    p.rope_n_pos = a.rope.rope_n_pos;
+    launch_fwd<true>(d.d, hp, g, p, stream);
   } else {
-    // head_dim 32: the D = 64 kernel on half-width heads
-    if (hp == 4) k_attn_fwd<64, 4, 32><<<g, kThreads, 0, stream>>>(p);
-    else if (hp == 2) k_attn_fwd<64, 2, 32><<<g, kThreads, 0, stream>>>(p);
-    else k_attn_fwd<64, 1, 32><<<g, kThreads, 0, stream>>>(p);
+    launch_fwd<false>(d.d, hp, g, p, stream);
   }
   return hipGetLastError();
 }

@@ -74,9 +74,37 @@ constexpr size_t kDebugTail = 256;
 constexpr size_t kDebugTail = 0;
 #endif
 
+// (cos, sin) table of the in-kernel rotary turns: positions [0, max_seqlen)
+// x head_dim / 2 frequencies, float2 each.
+size_t rope_table_bytes(const psc::AttnDims& d) {
+  return psc::align_up((size_t)d.max_seqlen * (size_t)(d.d / 2) * sizeof(float2), 256);
+}
+
+// Workspace of pass 0 (fwd), 1 (bwd), 2 (fwd with rotary turns), 3 (bwd with
+// rotary turns): the kernels' scratch, then the turn table (passes 2, 3),
+// then the debug flags word.
+size_t attn_part(int pass, int dtype, const psc::AttnDims& d) {
+  return pass % 2 == 0 ? psc::attn_fwd_workspace_bytes(dtype, d) : psc::attn_bwd_workspace_bytes(dtype, d);
+}
 size_t workspace_for(int pass, int dtype, const psc::AttnDims& d) {
-  return (pass == 0 ? psc::attn_fwd_workspace_bytes(dtype, d) : psc::attn_bwd_workspace_bytes(dtype, d)) +
-         kDebugTail;
+  return attn_part(pass, dtype, d) + (pass >= 2 ? rope_table_bytes(d) : 0) + kDebugTail;
+}
+
+// Checks of the rotary arguments of the fused entry points (host only).
+int rope_checks(int dtype, int32_t head_dim, const int32_t* positions, float base, int64_t T) {
+  if (!(base > 0.f) || std::isinf(base)) return PSC_ERR_INVALID;
+  if (T > 0 && !positions) return PSC_ERR_INVALID;
+  if (dtype != PSC_BF16 || (head_dim != 64 && head_dim != 128)) return PSC_ERR_UNSUPPORTED;
+  return PSC_OK;
+}
+
+psc::RopeArgs rope_args(int dtype, int32_t head_dim, float base) {
+  psc::RopeArgs a{};
+  a.dtype = dtype;
+  a.d = head_dim;
+  for (int i = 0; i < 64; ++i)
+    a.inv_freq[i] = i < head_dim / 2 ? std::pow((double)base, -2.0 * i / head_dim) : 0.0;
+  return a;
 }
 
 #ifdef PSC_DEBUG_CHECKS
@@ -111,9 +139,11 @@ int fwd_checks(int dtype, const void* q, const void* k, const void* v, int64_t q
 // Launch of a checked forward with a workspace of at least `need` bytes.
 int fwd_launch(int dtype, const psc::AttnDims& d, const void* q, const void* k, const void* v, int64_t sq, int64_t sk,
                int64_t sv, const int32_t* cu_seqlens, void* out, int64_t so, float* lse, void* workspace, size_t need,
-               hipStream_t stream) {
+               hipStream_t stream, const psc::AttnRope& rope = psc::AttnRope()) {
 #ifdef PSC_DEBUG_CHECKS
-  if (int c = debug_check_cu(cu_seqlens, d.n_seg, d.T, workspace, need, stream)) return c;
+  // need == 0: the caller ran the check before its own launches
+  if (need > 0)
+    if (int c = debug_check_cu(cu_seqlens, d.n_seg, d.T, workspace, need, stream)) return c;
 #else
   (void)need;
 #endif
@@ -130,7 +160,65 @@ int fwd_launch(int dtype, const psc::AttnDims& d, const void* q, const void* k, 
   a.out = out;
   a.lse = lse;
   a.workspace = workspace;
+  a.rope = rope;
   hipError_t e = dtype == PSC_BF16 ? psc::launch_attn_fwd_bf16(a, stream) : psc::launch_attn_fwd_f32(a, stream);
+  return e == hipSuccess ? PSC_OK : PSC_ERR_HIP;
+}
+
+// Argument checks of the backward (both entry points), host only.
+int bwd_checks(int dtype, int grad_dtype, const void* q, const void* k, const void* v, const void* out,
+               const void* dout, const float* lse, int64_t sq, int64_t sk, int64_t sv, int64_t so, int64_t sdo,
+               const int32_t* cu_seqlens, int32_t n_segments, int32_t max_seqlen, int64_t total_tokens, int32_t hq,
+               int32_t hkv, int32_t head_dim, float softmax_scale, const void* dq, const void* dk, const void* dv,
+               psc::AttnDims* d) {
+  int st = attn_dims(dtype, total_tokens, n_segments, max_seqlen, hq, hkv, head_dim, softmax_scale, d);
+  if (st != PSC_OK) return st;
+  if (grad_dtype != PSC_F32 && grad_dtype != PSC_BF16) return PSC_ERR_INVALID;
+  if (dtype == PSC_F32 && grad_dtype != PSC_F32) return PSC_ERR_UNSUPPORTED;
+  const int64_t T = total_tokens;
+  if (!operand_ok(q, sq, hq, head_dim, dtype, T) || !operand_ok(k, sk, hkv, head_dim, dtype, T) ||
+      !operand_ok(v, sv, hkv, head_dim, dtype, T) || !operand_ok(out, so, hq, head_dim, dtype, T) ||
+      !operand_ok(dout, sdo, hq, head_dim, dtype, T))
+    return PSC_ERR_INVALID;
+  if (T > 0 && (!cu_seqlens || !lse || !dq || !dk || !dv)) return PSC_ERR_INVALID;
+  if (T > 0 && ((reinterpret_cast<uintptr_t>(dq) | reinterpret_cast<uintptr_t>(dk) |
+                 reinterpret_cast<uintptr_t>(dv)) % 16 != 0))
+    return PSC_ERR_INVALID;
+  return PSC_OK;
+}
+
+int bwd_launch(int dtype, int grad_dtype, const psc::AttnDims& d, const void* q, const void* k, const void* v,
+               const void* out, const void* dout, const float* lse, int64_t sq, int64_t sk, int64_t sv, int64_t so,
+               int64_t sdo, const int32_t* cu_seqlens, void* dq, void* dk, void* dv, void* workspace, size_t need,
+               hipStream_t stream, const psc::AttnRope& rope = psc::AttnRope()) {
+#ifdef PSC_DEBUG_CHECKS
+  // need == 0: the caller ran the check before its own launches
+  if (need > 0)
+    if (int c = debug_check_cu(cu_seqlens, d.n_seg, d.T, workspace, need, stream)) return c;
+#else
+  (void)need;
+#endif
+  psc::AttnBwdArgs a;
+  a.dims = d;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = out;
+  a.dout = dout;
+  a.lse = lse;
+  a.sq = sq;
+  a.sk = sk;
+  a.sv = sv;
+  a.so = so;
+  a.sdo = sdo;
+  a.cu = cu_seqlens;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.grad_bf16 = grad_dtype == PSC_BF16;
+  a.workspace = workspace;
+  a.rope = rope;
+  hipError_t e = dtype == PSC_BF16 ? psc::launch_attn_bwd_bf16(a, stream) : psc::launch_attn_bwd_f32(a, stream);
   return e == hipSuccess ? PSC_OK : PSC_ERR_HIP;
 }
 
@@ -245,7 +333,7 @@ int psc_pack_build(int mode, const int32_t* tokens, const int64_t* doc_offsets, 
 
 int psc_varlen_attn_workspace(int pass, int dtype, int64_t total_tokens, int32_t n_segments, int32_t max_seqlen,
                               int32_t hq, int32_t hkv, int32_t head_dim, size_t* bytes) {
-  if (!bytes || (pass != 0 && pass != 1)) return PSC_ERR_INVALID;
+  if (!bytes || pass < 0 || pass > 3) return PSC_ERR_INVALID;
   psc::AttnDims d;
   int st = attn_dims(dtype, total_tokens, n_segments, max_seqlen, hq, hkv, head_dim, 0.f, &d);
   if (st != PSC_OK) return st;
@@ -298,50 +386,92 @@ int psc_varlen_attn_bwd(int dtype, int grad_dtype, const void* q, const void* k,
                         int32_t hq, int32_t hkv, int32_t head_dim, float softmax_scale, void* dq, void* dk,
                         void* dv, void* workspace, size_t workspace_bytes, void* stream) {
   psc::AttnDims d;
-  int st = attn_dims(dtype, total_tokens, n_segments, max_seqlen, hq, hkv, head_dim, softmax_scale, &d);
+  int st = bwd_checks(dtype, grad_dtype, q, k, v, out, dout, lse, q_tok_stride, k_tok_stride, v_tok_stride,
+                      out_tok_stride, dout_tok_stride, cu_seqlens, n_segments, max_seqlen, total_tokens, hq, hkv,
+                      head_dim, softmax_scale, dq, dk, dv, &d);
   if (st != PSC_OK) return st;
-  if (grad_dtype != PSC_F32 && grad_dtype != PSC_BF16) return PSC_ERR_INVALID;
-  if (dtype == PSC_F32 && grad_dtype != PSC_F32) return PSC_ERR_UNSUPPORTED;
-  const int64_t T = total_tokens;
-  if (!operand_ok(q, q_tok_stride, hq, head_dim, dtype, T) || !operand_ok(k, k_tok_stride, hkv, head_dim, dtype, T) ||
-      !operand_ok(v, v_tok_stride, hkv, head_dim, dtype, T) ||
-      !operand_ok(out, out_tok_stride, hq, head_dim, dtype, T) ||
-      !operand_ok(dout, dout_tok_stride, hq, head_dim, dtype, T))
-    return PSC_ERR_INVALID;
-  if (T > 0 && (!cu_seqlens || !lse || !dq || !dk || !dv)) return PSC_ERR_INVALID;
-  if (T > 0 && ((reinterpret_cast<uintptr_t>(dq) | reinterpret_cast<uintptr_t>(dk) |
-                 reinterpret_cast<uintptr_t>(dv)) % 16 != 0))
-    return PSC_ERR_INVALID;
   const size_t need = workspace_for(1, dtype, d);
+  if (total_tokens > 0 && (!workspace || workspace_bytes < need)) return PSC_ERR_WORKSPACE;
+  if (total_tokens == 0) return PSC_OK;
+  return bwd_launch(dtype, grad_dtype, d, q, k, v, out, dout, lse, q_tok_stride, k_tok_stride, v_tok_stride,
+                    out_tok_stride, dout_tok_stride, cu_seqlens, dq, dk, dv, workspace, need,
+                    static_cast<hipStream_t>(stream));
+}
+
+int psc_varlen_attn_fwd_rope(int dtype, void* q, void* k, const void* v, int64_t q_tok_stride, int64_t k_tok_stride,
+                             int64_t v_tok_stride, const int32_t* cu_seqlens, int32_t n_segments, int32_t max_seqlen,
+                             int64_t total_tokens, int32_t hq, int32_t hkv, int32_t head_dim,
+                             const int32_t* positions, float rope_base, float softmax_scale, void* out,
+                             int64_t out_tok_stride, float* lse, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  psc::AttnDims d;
+  int st = fwd_checks(dtype, q, k, v, q_tok_stride, k_tok_stride, v_tok_stride, cu_seqlens, n_segments, max_seqlen,
+                      total_tokens, hq, hkv, head_dim, softmax_scale, out, out_tok_stride, lse, &d);
+  if (st != PSC_OK) return st;
+  st = rope_checks(dtype, head_dim, positions, rope_base, total_tokens);
+  if (st != PSC_OK) return st;
+  const int64_t T = total_tokens;
+  const size_t need = workspace_for(2, dtype, d);
   if (T > 0 && (!workspace || workspace_bytes < need)) return PSC_ERR_WORKSPACE;
   if (T == 0) return PSC_OK;
-#ifdef PSC_DEBUG_CHECKS
-  if (int c = debug_check_cu(cu_seqlens, n_segments, T, workspace, need, static_cast<hipStream_t>(stream)))
-    return c;
-#endif
-
-  psc::AttnBwdArgs a;
-  a.dims = d;
-  a.q = q;
-  a.k = k;
-  a.v = v;
-  a.o = out;
-  a.dout = dout;
-  a.lse = lse;
-  a.sq = q_tok_stride;
-  a.sk = k_tok_stride;
-  a.sv = v_tok_stride;
-  a.so = out_tok_stride;
-  a.sdo = dout_tok_stride;
-  a.cu = cu_seqlens;
-  a.dq = dq;
-  a.dk = dk;
-  a.dv = dv;
-  a.grad_bf16 = grad_dtype == PSC_BF16;
-  a.workspace = workspace;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = dtype == PSC_BF16 ? psc::launch_attn_bwd_bf16(a, s) : psc::launch_attn_bwd_f32(a, s);
-  return e == hipSuccess ? PSC_OK : PSC_ERR_HIP;
+#ifdef PSC_DEBUG_CHECKS
+  if (int c = debug_check_cu(cu_seqlens, n_segments, T, workspace, need, s)) return c;
+#endif
+  // the turn table, then k turned in place by the rotation kernel; q is
+  // turned inside the attention kernel as it is loaded, and written back
+  float2* table = reinterpret_cast<float2*>(static_cast<char*>(workspace) + attn_part(2, dtype, d));
+  psc::RopeArgs ra = rope_args(dtype, head_dim, rope_base);
+  ra.T = T;
+  ra.pos = positions;
+  if (psc::launch_rope_table(ra, d.max_seqlen, table, s) != hipSuccess) return PSC_ERR_HIP;
+  psc::RopeArgs rk = ra;
+  rk.q = k;
+  rk.sq = k_tok_stride;
+  rk.hq = hkv;
+  rk.k = nullptr;
+  rk.sk = 0;
+  rk.hkv = 0;
+  rk.inverse = 0;
+  if (psc::launch_rope(rk, s) != hipSuccess) return PSC_ERR_HIP;
+  psc::AttnRope rope;
+  rope.pos = positions;
+  rope.rope_cs = table;
+  rope.rope_n_pos = d.max_seqlen;
+  return fwd_launch(dtype, d, q, k, v, q_tok_stride, k_tok_stride, v_tok_stride, cu_seqlens, out, out_tok_stride,
+                    lse, workspace, 0, s, rope);
+}
+
+int psc_varlen_attn_bwd_rope(int dtype, int grad_dtype, const void* q_rot, const void* k_rot, const void* v,
+                             const void* out, const void* dout, const float* lse, int64_t q_tok_stride,
+                             int64_t k_tok_stride, int64_t v_tok_stride, int64_t out_tok_stride,
+                             int64_t dout_tok_stride, const int32_t* cu_seqlens, int32_t n_segments,
+                             int32_t max_seqlen, int64_t total_tokens, int32_t hq, int32_t hkv, int32_t head_dim,
+                             const int32_t* positions, float rope_base, float softmax_scale, void* dq, void* dk,
+                             void* dv, void* workspace, size_t workspace_bytes, void* stream) {
+  psc::AttnDims d;
+  int st = bwd_checks(dtype, grad_dtype, q_rot, k_rot, v, out, dout, lse, q_tok_stride, k_tok_stride, v_tok_stride,
+                      out_tok_stride, dout_tok_stride, cu_seqlens, n_segments, max_seqlen, total_tokens, hq, hkv,
+                      head_dim, softmax_scale, dq, dk, dv, &d);
+  if (st != PSC_OK) return st;
+  st = rope_checks(dtype, head_dim, positions, rope_base, total_tokens);
+  if (st != PSC_OK) return st;
+  const size_t need = workspace_for(3, dtype, d);
+  if (total_tokens > 0 && (!workspace || workspace_bytes < need)) return PSC_ERR_WORKSPACE;
+  if (total_tokens == 0) return PSC_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+#ifdef PSC_DEBUG_CHECKS
+  if (int c = debug_check_cu(cu_seqlens, n_segments, total_tokens, workspace, need, s)) return c;
+#endif
+  float2* table = reinterpret_cast<float2*>(static_cast<char*>(workspace) + attn_part(3, dtype, d));
+  psc::RopeArgs ra = rope_args(dtype, head_dim, rope_base);
+  if (psc::launch_rope_table(ra, d.max_seqlen, table, s) != hipSuccess) return PSC_ERR_HIP;
+  psc::AttnRope rope;
+  rope.pos = positions;
+  rope.rope_cs = table;
+  rope.rope_n_pos = d.max_seqlen;
+  return bwd_launch(dtype, grad_dtype, d, q_rot, k_rot, v, out, dout, lse, q_tok_stride, k_tok_stride, v_tok_stride,
+                    out_tok_stride, dout_tok_stride, cu_seqlens, dq, dk, dv, workspace, 0, s, rope);
 }
 
 int psc_check_cu_seqlens(const int32_t* cu_seqlens, int32_t n_segments, int64_t total_tokens, int32_t* flags,

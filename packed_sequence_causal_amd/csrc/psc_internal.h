@@ -65,6 +65,15 @@ struct AttnDims {
   float scale;  // softmax scale (natural units)
 };
 
+// Rotary embedding inside the attention kernels (null rope_cs: none).
+// rope_cs[pos * D/2 + i] = (cos, sin) of the turn of dims (i, i + D/2) at
+// position pos < rope_n_pos; pos = positions[token], clamped to the table.
+struct AttnRope {
+  const int32_t* pos = nullptr;
+  const float2* rope_cs = nullptr;
+  int32_t rope_n_pos = 0;
+};
+
 struct AttnFwdArgs {
   AttnDims dims;
   const void *q, *k, *v;
@@ -73,6 +82,7 @@ struct AttnFwdArgs {
   void* out;
   float* lse;
   void* workspace;
+  AttnRope rope;  // with rope: q is turned in registers and written back in place
 };
 
 struct AttnBwdArgs {
@@ -84,6 +94,7 @@ struct AttnBwdArgs {
   void *dq, *dk, *dv;  // float32, or bf16 when grad_bf16 (bf16 inputs only)
   int32_t grad_bf16;
   void* workspace;
+  AttnRope rope;  // with rope: dq and dk are turned back (by -theta) before they are stored
 };
 
 // Work list of (segment, tile) pairs, most work first (attn_sched.hip).
@@ -120,6 +131,8 @@ struct RopeArgs {
   double inv_freq[64];  // base^(-2i/D), i < D/2
 };
 hipError_t launch_rope(const RopeArgs& a, hipStream_t stream);
+// (cos, sin) table of positions [0, n_pos) for the attention kernels' turns.
+hipError_t launch_rope_table(const RopeArgs& a, int32_t n_pos, float2* table, hipStream_t stream);
 
 // unpack_data of packed rows [n_rows, packed_len] with the packer's flattened
 // cu_seqlens (n_cu entries), row_seg_ptr and row_valid_len.

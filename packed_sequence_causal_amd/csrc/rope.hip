@@ -12,16 +12,15 @@
 // on an argument in [-pi, pi].
 #include "attn_common.h"
 #include "psc_internal.h"
+#include "rope_common.h"
 
+#include <algorithm>
 #include <type_traits>
 
 namespace psc {
 namespace {
 
 constexpr int kRopeThreads = 256;
-constexpr double kTwoPiHi = 6.283185307179586;        // nearest double to 2*pi
-constexpr double kTwoPiLo = 2.4492935982947064e-16;   // 2*pi - kTwoPiHi
-constexpr double kInvTwoPi = 0.15915494309189535;
 
 template <typename E>
 struct Vec16;
@@ -55,15 +54,9 @@ __global__ void __launch_bounds__(kRopeThreads) k_rope(RopeArgs a) {
   for (int x = threadIdx.x; x < kTokPerWg * (D / 2); x += kRopeThreads) {
     const int tk = x / (D / 2), i = x % (D / 2);
     float c = 1.f, sv = 0.f;
-    if (tk < ntok) {
-      const double th = (double)a.pos[t0 + tk] * a.inv_freq[i];
-      const double k = rint(th * kInvTwoPi);
-      double r = fma(-k, kTwoPiHi, th);
-      r = fma(-k, kTwoPiLo, r);
-      sincosf((float)r, &sv, &c);
-    }
+    if (tk < ntok) rope_cs(a.pos[t0 + tk], a.inv_freq[i], a.inverse != 0, c, sv);
     cs_s[tk][i] = c;
-    sn_s[tk][i] = a.inverse ? -sv : sv;
+    sn_s[tk][i] = sv;
   }
   __syncthreads();
   // chunk index: token-major, then q heads then k heads, then chunk in head
@@ -97,9 +90,10 @@ __global__ void __launch_bounds__(kRopeThreads) k_rope(RopeArgs a) {
 #pragma unroll
       for (int e = 0; e < PP; ++e) {
         const float c = cs_s[tkk[u]][ii[u] + e], sv = sn_s[tkk[u]][ii[u] + e];
-        const float a1 = (float)x1[u][e], a2 = (float)x2[u][e];
-        y1[e] = (E)__builtin_fmaf(a1, c, -a2 * sv);
-        y2[e] = (E)__builtin_fmaf(a2, c, a1 * sv);
+        float r1, r2;
+        rope_turn((float)x1[u][e], (float)x2[u][e], c, sv, r1, r2);
+        y1[e] = (E)r1;
+        y2[e] = (E)r2;
       }
       *reinterpret_cast<V*>(ptr[u]) = y1;
       *reinterpret_cast<V*>(ptr[u] + D / 2) = y2;
@@ -114,7 +108,30 @@ hipError_t launch_typed(const RopeArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// cos and sin of every (position, frequency) pair for positions [0, n_pos):
+// table[pos * (D/2) + i] = (cos, sin) of pos * inv_freq[i], the turn the
+// attention kernels apply inside their loads and epilogues.
+__global__ void __launch_bounds__(kRopeThreads) k_rope_table(RopeArgs a, int32_t n_pos, float2* table) {
+  const int half = a.d / 2;
+  const int64_t n = (int64_t)n_pos * half;
+  for (int64_t x = (int64_t)blockIdx.x * kRopeThreads + threadIdx.x; x < n; x += (int64_t)gridDim.x * kRopeThreads) {
+    const int32_t pos = (int32_t)(x / half);
+    const int i = (int)(x - (int64_t)pos * half);
+    float c, sv;
+    rope_cs(pos, a.inv_freq[i], false, c, sv);
+    table[x] = make_float2(c, sv);
+  }
+}
+
 }  // namespace
+
+hipError_t launch_rope_table(const RopeArgs& a, int32_t n_pos, float2* table, hipStream_t stream) {
+  const int64_t n = (int64_t)n_pos * (a.d / 2);
+  if (n == 0) return hipSuccess;
+  const unsigned blocks = (unsigned)std::min<int64_t>((n + kRopeThreads - 1) / kRopeThreads, 4096);
+  k_rope_table<<<blocks, kRopeThreads, 0, stream>>>(a, n_pos, table);
+  return hipGetLastError();
+}
 
 hipError_t launch_rope(const RopeArgs& a, hipStream_t stream) {
   if (a.T == 0) return hipSuccess;

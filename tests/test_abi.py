@@ -226,8 +226,13 @@ def test_attn_workspace_sizes():
     bwd = psc.varlen_attn_workspace(1, psc.BF16, 65536, 48, 4654, 32, 8, 128)
     assert 0 < fwd < (1 << 20)
     assert bwd >= 4 * 32 * 65536  # D row sums in fp32
-    with pytest.raises(psc.PscError):
-        psc.varlen_attn_workspace(2, psc.BF16, 16, 1, 16, 2, 1, 128)
+    # the fused-rotary passes add the (cos, sin) table: max_seqlen x D/2 float2
+    fr = psc.varlen_attn_workspace(2, psc.BF16, 65536, 48, 4654, 32, 8, 128)
+    br = psc.varlen_attn_workspace(3, psc.BF16, 65536, 48, 4654, 32, 8, 128)
+    assert fr >= fwd + 4654 * 64 * 8 and br >= bwd + 4654 * 64 * 8
+    for bad in (4, -1):
+        with pytest.raises(psc.PscError):
+            psc.varlen_attn_workspace(bad, psc.BF16, 16, 1, 16, 2, 1, 128)
 
 
 def _rope_raw(**kw):
@@ -316,3 +321,45 @@ def test_noalloc_forward_rejects_sizes_beyond_its_scratch():
                                          1024, v, None) == psc.ERR_INVALID
     assert L.psc_varlen_attn_fwd_noalloc(psc.BF16, v, v, v, 1024, 256, 256, v, 1, 16, 16, 8, 2, 96, 0.0, v, 1024,
                                          v, None) == psc.ERR_UNSUPPORTED
+
+
+def _rope_fwd_raw(**kw):
+    a = dict(dtype=psc.BF16, q=16, k=16, v=16, sq=256, sk=128, sv=128, cu=16, nseg=1, maxlen=16, T=16, hq=2, hkv=1,
+             d=128, pos=16, base=10000.0, scale=0.0, out=16, so=256, lse=16, ws=16, wsb=8)
+    a.update(kw)
+    v = lambda x: None if x is None else ctypes.c_void_p(x)
+    return psc.lib().psc_varlen_attn_fwd_rope(a["dtype"], v(a["q"]), v(a["k"]), v(a["v"]), a["sq"], a["sk"], a["sv"],
+                                              v(a["cu"]), a["nseg"], a["maxlen"], a["T"], a["hq"], a["hkv"], a["d"],
+                                              v(a["pos"]), a["base"], a["scale"], v(a["out"]), a["so"], v(a["lse"]),
+                                              v(a["ws"]), a["wsb"], None)
+
+
+# every case has too small a workspace (8 bytes): nothing can be launched on
+# these fake pointers even if the check under test were missing
+@pytest.mark.parametrize("kw,code", [
+    (dict(), psc.ERR_WORKSPACE),                       # otherwise valid
+    (dict(dtype=psc.F32, sq=256, sk=128, sv=128), psc.ERR_UNSUPPORTED),  # fp32 inputs
+    (dict(d=32, sq=64, sk=32, sv=32, so=64), psc.ERR_UNSUPPORTED),      # head_dim 32
+    (dict(pos=None), psc.ERR_INVALID),
+    (dict(base=0.0), psc.ERR_INVALID),
+    (dict(base=float("nan")), psc.ERR_INVALID),
+    (dict(q=None), psc.ERR_INVALID),
+])
+def test_attn_fwd_rope_rejects_on_host(kw, code):
+    assert _rope_fwd_raw(**kw) == code
+
+
+def test_attn_bwd_rope_rejects_on_host():
+    v = lambda x: None if x is None else ctypes.c_void_p(x)
+    L = psc.lib()
+    base = [psc.BF16, psc.F32, v(16), v(16), v(16), v(16), v(16), v(16), 256, 128, 128, 256, 256, v(16), 1, 16, 16,
+            2, 1, 128, v(16), 10000.0, 0.0, v(16), v(16), v(16), v(16), 8, None]
+    assert L.psc_varlen_attn_bwd_rope(*base) == psc.ERR_WORKSPACE
+    for idx, val, code in ((20, None, psc.ERR_INVALID), (21, -1.0, psc.ERR_INVALID), (19, 64, psc.ERR_WORKSPACE),
+                           (1, 7, psc.ERR_INVALID)):
+        bad = list(base)
+        bad[idx] = val
+        assert L.psc_varlen_attn_bwd_rope(*bad) == code, (idx, val)
+    f32 = list(base)
+    f32[0] = psc.F32
+    assert L.psc_varlen_attn_bwd_rope(*f32) == psc.ERR_UNSUPPORTED
