@@ -42,15 +42,18 @@ BF16_WORKLOADS = ["lognormal_32k", "uniform_8k", "seqpar_share_128k", "skewed_32
 # WRITE_SIZE), for (kernel, workload), valid only while the kernel's sources
 # hash to the recorded value (profiles/hbm_counters_<workload>.md).
 KERNEL_SOURCES = {
-    "attn_fwd": ["packed_sequence_causal_amd/csrc/attn_fwd.hip", "packed_sequence_causal_amd/csrc/attn_common.h"],
-    "attn_bwd_dkdv": ["packed_sequence_causal_amd/csrc/attn_bwd.hip", "packed_sequence_causal_amd/csrc/attn_common.h"],
-    "attn_bwd_dq": ["packed_sequence_causal_amd/csrc/attn_bwd.hip", "packed_sequence_causal_amd/csrc/attn_common.h"],
+    "attn_fwd": ["packed_sequence_causal_amd/csrc/attn_fwd.hip", "packed_sequence_causal_amd/csrc/attn_common.h",
+                 "packed_sequence_causal_amd/csrc/rope_common.h"],
+    "attn_bwd_dkdv": ["packed_sequence_causal_amd/csrc/attn_bwd.hip", "packed_sequence_causal_amd/csrc/attn_common.h",
+                      "packed_sequence_causal_amd/csrc/rope_common.h"],
+    "attn_bwd_dq": ["packed_sequence_causal_amd/csrc/attn_bwd.hip", "packed_sequence_causal_amd/csrc/attn_common.h",
+                    "packed_sequence_causal_amd/csrc/rope_common.h"],
 }
 MEASURED_TRAFFIC = {
     # (kernel, workload): (sources sha256 prefix, read bytes, write bytes)
-    ("attn_fwd", "lognormal_32k"): ("17033b393f969993", 2.0 * 420369.4 * 1024, 1.0 * 533396.8 * 1024),
-    ("attn_bwd_dkdv", "lognormal_32k"): ("0171924ac3e7b751", 2.0 * 4199159.2 * 1024, 1.0 * 532863.5 * 1024),
-    ("attn_bwd_dq", "lognormal_32k"): ("0171924ac3e7b751", 2.0 * 967306.0 * 1024, 1.0 * 1065907.8 * 1024),
+    ("attn_fwd", "lognormal_32k"): ("2290f70f7c66f31f", 2.0 * 418320.5 * 1024, 1.0 * 533332.2 * 1024),
+    ("attn_bwd_dkdv", "lognormal_32k"): ("8ef2a2d29357273e", 2.0 * 4190203.7 * 1024, 1.0 * 532863.9 * 1024),
+    ("attn_bwd_dq", "lognormal_32k"): ("8ef2a2d29357273e", 2.0 * 965065.4 * 1024, 1.0 * 1066041.2 * 1024),
 }
 
 
@@ -82,6 +85,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-other-workloads", action="store_true",
                     help="time only --workload (by default the line also carries every other bf16 workload)")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the separate RoPE, fused-RoPE step and data-step measurements (profiles of the "
+                         "step's own kernels use this)")
     ap.add_argument("--doc-sweep", action="store_true",
                     help="time each 32K document layout with its document mask and as one whole-row causal "
                          "segment (same kernels); one JSON line per layout")
@@ -545,9 +551,10 @@ def main():
     }
     if a.backward:
         result["bwd"] = summ["bwd"]
-    result["rope"] = rope_rate(psc, torch, np, ctx["qd"], ctx["kd"], ctx["pk"], w, args)
-    result["rope_step"] = rope_step_rate(psc, torch, np, ctx, w, min(args.steps, 10))
-    result["data_steps"] = data_steps_rate(psc, torch, np, ctx["pk"], w)
+    if not args.no_extras:
+        result["rope"] = rope_rate(psc, torch, np, ctx["qd"], ctx["kd"], ctx["pk"], w, args)
+        result["rope_step"] = rope_step_rate(psc, torch, np, ctx, w, min(args.steps, 10))
+        result["data_steps"] = data_steps_rate(psc, torch, np, ctx["pk"], w)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, ctx["q"], ctx["k"], ctx["v"], ctx["do"], ctx["cu_h"], ctx["real"],
                                               args.cpu_seconds)
