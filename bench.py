@@ -17,7 +17,16 @@ Prints one JSON line.  Besides the standard fields it carries
                 summed over the timed steps) against the bf16 MFMA peak;
   cpu_baseline: the fp64 CPU oracle timed on a bounded sample of the same
                 workload (whole documents in order until ~--cpu-seconds of
-                work), in the same unit.
+                work), in the same unit;
+  clock:        graphics clock and socket power read with amd-smi while the
+                step loops after the timed region, and the rate against the
+                peak at that clock;
+  workloads:    the same step on every other bf16 workload;
+  seed1:        the default workload drawn from seed 1;
+  rope, rope_step, data_steps: the rotary embedding pass, the step with the
+                rotation separate and fused, and the packer's follow-up data
+                steps.
+Defaults: 10 untimed warm-up steps, then 50 timed steps.
 """
 import argparse
 import json
@@ -77,14 +86,15 @@ def measured_traffic(kernel, workload):
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="lognormal_32k")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the CPU oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-other-workloads", action="store_true",
                     help="time only --workload (by default the line also carries every other bf16 workload)")
+    ap.add_argument("--no-clock", action="store_true", help="skip the amd-smi clock and power reading")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the separate RoPE, fused-RoPE step and data-step measurements (profiles of the "
                          "step's own kernels use this)")
@@ -480,8 +490,61 @@ def measure(w, args, steps, warmup, torch, np, psc):
                           "pct_peak": round(100 * bwd_flops / (bwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2)}
     ctx = dict(q=q, k=k, v=v, do=do, qd=qd, kd=kd, vd=vd, dod=dod, pk=pk, cu=cu, cu_h=cu_h, n_seg=n_seg,
                max_seqlen=max_seqlen, real=real, kt=kt, ms=ms, value=value, fwd_flops=fwd_flops,
-               bwd_flops=bwd_flops)
+               bwd_flops=bwd_flops, step=step)
     return summary, ctx
+
+
+def sustained_clock(step, torch, value):
+    """Graphics clock and socket power while the step runs back to back,
+    outside the timed region: `amd-smi metric -p -c` is read twice (per-XCD
+    GFX clocks, socket power) while the loop keeps the GPU busy, and `value`
+    is restated against the bf16 peak scaled to the mean clock read.  None
+    where amd-smi is not installed or prints neither figure."""
+    import re
+    import shutil
+    import subprocess
+    import threading
+
+    exe = shutil.which("amd-smi")
+    if exe is None:
+        return None
+    outs = []
+
+    def poll():
+        for _ in range(2):
+            try:
+                outs.append(subprocess.run([exe, "metric", "-p", "-c"], capture_output=True, text=True,
+                                           timeout=30).stdout)
+            except (OSError, subprocess.SubprocessError):
+                pass
+
+    t_end = time.perf_counter() + 0.5  # clocks settle under load before the first read
+    n = 0
+    while time.perf_counter() < t_end:
+        step()
+        n += 1
+        if n % 8 == 0:
+            torch.cuda.synchronize()
+    th = threading.Thread(target=poll)
+    th.start()
+    while th.is_alive():
+        step()
+        n += 1
+        if n % 8 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    clk = [int(m) for o in outs for m in re.findall(r"GFX_\d+:\s*\n\s*CLK:\s*(\d+)\s*MHz", o)]
+    pw = [int(m) for o in outs for m in re.findall(r"SOCKET_POWER:\s*(\d+)\s*W", o)]
+    if not clk and not pw:
+        return None
+    res = {"source": "amd-smi metric -p -c, twice, while the step loops (untimed)", "steps_run": n,
+           "socket_power_w": pw}
+    if clk:
+        mhz = sum(clk) / len(clk)
+        res.update({"gfx_mhz_mean": round(mhz, 1), "gfx_mhz_min": min(clk), "gfx_mhz_max": max(clk),
+                    "peak_at_clock_tflops": round(PEAK_BF16_TFLOPS * mhz / 2400.0, 1),
+                    "pct_peak_at_clock": round(100 * value / (PEAK_BF16_TFLOPS * mhz / 2400.0), 2)})
+    return res
 
 
 def main():
@@ -551,6 +614,8 @@ def main():
     }
     if a.backward:
         result["bwd"] = summ["bwd"]
+    if not args.no_clock:
+        result["clock"] = sustained_clock(ctx["step"], torch, summ["tflops"])
     if not args.no_extras:
         result["rope"] = rope_rate(psc, torch, np, ctx["qd"], ctx["kd"], ctx["pk"], w, args)
         result["rope_step"] = rope_step_rate(psc, torch, np, ctx, w, min(args.steps, 10))
@@ -568,11 +633,17 @@ def main():
                 continue
             torch.cuda.empty_cache()
             wo = workloads.make(name, args.seed)
-            s_o, _ = measure(wo, args, min(args.steps, 10), min(args.warmup, 3), torch, np, psc)
+            s_o, _ = measure(wo, args, args.steps, args.warmup, torch, np, psc)
             others[name] = s_o
             print(f"# {name}: {s_o['ms_per_step']} ms/step, fwd {s_o['fwd']['pct_peak']} %"
                   + (f", bwd {s_o['bwd']['pct_peak']} %" if "bwd" in s_o else ""), file=sys.stderr, flush=True)
         result["workloads"] = others
+    # the same workload drawn from seed 1 (document lengths and values)
+    if not args.no_other_workloads and args.seed == 0:
+        torch.cuda.empty_cache()
+        s_1, _ = measure(workloads.make(w.name, 1), args, args.steps, args.warmup, torch, np, psc)
+        s_1["seed"] = 1
+        result["seed1"] = s_1
     print(json.dumps(result), flush=True)
 
 
