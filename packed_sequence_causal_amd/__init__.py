@@ -4,6 +4,8 @@ Thin ctypes binding over ``libpsc.so`` (C ABI in ``include/psc.h``).  It only
 marshals arguments: torch tensors provide device memory and the current HIP
 stream; every step of the computation runs in the library's HIP kernels.
 There is no fallback: without the built library every call raises.
+``PSC_LIBRARY`` (environment) names another build of the library to load
+instead of the in-tree ``libpsc.so`` (the host-sanitizer test uses it).
 
 Entry points (same names as the C ABI without the ``psc_`` prefix):
   pack_sizes, pack_build                  build_pack / build_unpack on the GPU
@@ -36,7 +38,7 @@ ERR_CAPACITY = -4
 ERR_HIP = -5
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libpsc.so")
+LIB_PATH = os.environ.get("PSC_LIBRARY") or os.path.join(_HERE, "libpsc.so")
 DEBUG_LIB_PATH = os.path.join(_HERE, "libpsc_debug.so")
 _libs = {}
 

@@ -1,7 +1,8 @@
 """Build libpsc.so in-tree with hipcc for gfx950.
 
-    python -m packed_sequence_causal_amd.build          # release library
-    python -m packed_sequence_causal_amd.build --debug  # also libpsc_debug.so
+    python -m packed_sequence_causal_amd.build             # release library
+    python -m packed_sequence_causal_amd.build --debug     # also libpsc_debug.so
+    python -m packed_sequence_causal_amd.build --sanitize  # also libpsc_san.so
 
 Every HIP source under csrc/ is compiled to an object in csrc/../_build and
 linked into packed_sequence_causal_amd/libpsc.so.  The debug variant
@@ -9,6 +10,13 @@ linked into packed_sequence_causal_amd/libpsc.so.  The debug variant
 PSC_DEBUG_CHECKS: its attention calls validate cu_seqlens on the device before
 launching.  Packed-fp32 instruction selection is switched off for all device
 code.
+
+The sanitizer variant (objects in _build_san, library libpsc_san.so) is the
+same code with its host side built with AddressSanitizer and
+UndefinedBehaviorSanitizer (device code as in the release library): it puts
+argument checks, sizing and workspace carving under the sanitizers, on a
+machine without a GPU.  It loads only with the ASan runtime preloaded
+(asan_runtime()).
 """
 from __future__ import annotations
 
@@ -25,6 +33,11 @@ LIB = os.path.join(PKG, "libpsc.so")
 BUILD_DEBUG = os.path.join(PKG, "_build_debug")
 LIB_DEBUG = os.path.join(PKG, "libpsc_debug.so")
 ARCH = os.environ.get("PSC_OFFLOAD_ARCH", "gfx950")
+BUILD_SAN = os.path.join(PKG, "_build_san")
+LIB_SAN = os.path.join(PKG, "libpsc_san.so")
+# every sanitizer flag is host-side only
+SAN_FLAGS = ("-Xarch_host -g -Xarch_host -fsanitize=address -Xarch_host -fsanitize=undefined "
+             "-Xarch_host -fno-sanitize-recover=undefined -Xarch_host -fno-omit-frame-pointer").split()
 
 COMMON = [
     f"--offload-arch={ARCH}",
@@ -68,11 +81,35 @@ def _link(objs, lib):
     os.replace(tmp, lib)
 
 
-def build(verbose: bool = False, debug: bool = False) -> str:
-    """Compile and link libpsc.so (and libpsc_debug.so when debug=True)."""
-    variants = [(BUILD, LIB, [])]
+def stale(lib: str) -> bool:
+    """True when `lib` is missing or older than a source or header it is built from."""
+    if not os.path.exists(lib):
+        return True
+    t = os.path.getmtime(lib)
+    inc = os.path.join(PKG, "..", "include")
+    deps = [os.path.join(CSRC, f) for f in os.listdir(CSRC)] + [os.path.join(inc, f) for f in os.listdir(inc)]
+    return any(os.path.getmtime(f) > t for f in deps)
+
+
+def asan_runtime() -> str:
+    """Path of the ASan runtime (with the UBSan handlers) that a process
+    loading libpsc_san.so must preload."""
+    r = subprocess.run([_hipcc(), "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True,
+                       text=True)
+    path = r.stdout.strip()
+    if r.returncode != 0 or not os.path.isabs(path) or not os.path.exists(path):
+        raise RuntimeError(f"ASan runtime not found ({path!r})")
+    return path
+
+
+def build(verbose: bool = False, debug: bool = False, sanitize: bool = False, release: bool = True) -> str:
+    """Compile and link libpsc.so (unless release=False), libpsc_debug.so when
+    debug=True and libpsc_san.so when sanitize=True."""
+    variants = [(BUILD, LIB, [])] if release else []
     if debug:
         variants.append((BUILD_DEBUG, LIB_DEBUG, ["-DPSC_DEBUG_CHECKS"]))
+    if sanitize:
+        variants.append((BUILD_SAN, LIB_SAN, SAN_FLAGS))
     jobs = []
     for outdir, _, extra in variants:
         os.makedirs(outdir, exist_ok=True)
@@ -85,10 +122,10 @@ def build(verbose: bool = False, debug: bool = False) -> str:
             lines = [ln for ln in err.splitlines() if "packed-fp32-ops" not in ln and ln.strip()]
             if lines:
                 print("\n".join(lines), file=sys.stderr)
-    for outdir, lib, _ in variants:
+    for outdir, lib, extra in variants:
         _link([o for o, _ in results if os.path.dirname(o) == outdir], lib)
     return LIB
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv, debug="--debug" in sys.argv))
+    print(build(verbose="-v" in sys.argv, debug="--debug" in sys.argv, sanitize="--sanitize" in sys.argv))
