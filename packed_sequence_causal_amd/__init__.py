@@ -204,8 +204,7 @@ def pack_build(tokens, doc_offsets, micro_bsz: int, seq_len: int, mode: int = PA
                 "row_valid_len": torch.empty(max(rows, 1), **i32),
                 "stats": torch.empty(4, **i32),
             }
-        if workspace is None:
-            workspace = torch.empty(max(ws, 256), dtype=torch.uint8, device=dev)
+        workspace = _workspace(workspace, ws, dev)
     _check(lib().psc_pack_build(mode, _ptr(tokens), _ptr(doc_offsets), n_docs, n_tokens, micro_bsz, seq_len,
                                 rows, _ptr(out["input_ids"]), _ptr(out["labels"]), _ptr(out["indexes"]),
                                 _ptr(out["cu_seqlens"]), out["cu_seqlens"].numel() - 1,
@@ -234,11 +233,29 @@ def _tok_stride(t, name):
 
 
 def varlen_attn_workspace(pass_: int, dtype: int, total_tokens: int, n_segments: int, max_seqlen: int,
-                          hq: int, hkv: int, head_dim: int) -> int:
+                          hq: int, hkv: int, head_dim: int, library=None) -> int:
+    """Workspace bytes of pass 0 (forward), 1 (backward), 2 (rotary forward)
+    or 3 (rotary backward); `library` as in the calls (the debug library's
+    are longer)."""
     b = ctypes.c_size_t()
-    _check(lib().psc_varlen_attn_workspace(pass_, dtype, total_tokens, n_segments, max_seqlen, hq, hkv, head_dim,
+    _check((library or lib()).psc_varlen_attn_workspace(pass_, dtype, total_tokens, n_segments, max_seqlen, hq, hkv, head_dim,
                                            ctypes.byref(b)), "psc_varlen_attn_workspace")
     return b.value
+
+
+def _workspace(workspace, need: int, device):
+    """The caller's workspace, checked, or a new one of `need` bytes (on the
+    current stream: call inside the stream context)."""
+    import torch
+
+    if workspace is None:
+        return torch.empty(max(need, 256), dtype=torch.uint8, device=device)
+    if (workspace.dtype != torch.uint8 or workspace.dim() != 1 or not workspace.is_contiguous()
+            or workspace.device != device):
+        raise ValueError(f"workspace must be a contiguous 1-D uint8 tensor on {device}")
+    if workspace.numel() < need:
+        raise ValueError(f"workspace holds {workspace.numel()} bytes; this call needs {need}")
+    return workspace
 
 
 def _check_inputs(q, k, v, cu_seqlens, nseg):
@@ -278,8 +295,7 @@ def varlen_attn_fwd(q, k, v, cu_seqlens, max_seqlen: int, n_segments: Optional[i
             out = torch.empty(T, hq, D, dtype=q.dtype, device=q.device)
         if lse is None:
             lse = torch.empty(hq, T, dtype=torch.float32, device=q.device)
-        if workspace is None or workspace.numel() < ws:
-            workspace = torch.empty(max(ws, 256), dtype=torch.uint8, device=q.device)
+        workspace = _workspace(workspace, ws, q.device)
     if out.dim() != 3 or tuple(out.shape) != (T, hq, D) or out.dtype != q.dtype or out.device != q.device:
         raise ValueError(f"out must be a {q.dtype} [T, hq, D] = {(T, hq, D)} tensor on {q.device}")
     _expect(lse, "lse", (hq, T), torch.float32, q.device)
@@ -346,8 +362,7 @@ def varlen_attn_bwd(q, k, v, out, dout, lse, cu_seqlens, max_seqlen: int, n_segm
         dq = torch.empty(T, hq, D, **g) if dq is None else dq
         dk = torch.empty(T, hkv, D, **g) if dk is None else dk
         dv = torch.empty(T, hkv, D, **g) if dv is None else dv
-        if workspace is None or workspace.numel() < ws:
-            workspace = torch.empty(max(ws, 256), dtype=torch.uint8, device=q.device)
+        workspace = _workspace(workspace, ws, q.device)
     _expect(dq, "dq", (T, hq, D), gtype, q.device)
     _expect(dk, "dk", (T, hkv, D), gtype, q.device)
     _expect(dv, "dv", (T, hkv, D), gtype, q.device)
@@ -388,8 +403,7 @@ def varlen_attn_fwd_rope(q, k, v, cu_seqlens, max_seqlen: int, positions, rope_b
             out = torch.empty(T, hq, D, dtype=q.dtype, device=q.device)
         if lse is None:
             lse = torch.empty(hq, T, dtype=torch.float32, device=q.device)
-        if workspace is None or workspace.numel() < ws:
-            workspace = torch.empty(max(ws, 256), dtype=torch.uint8, device=q.device)
+        workspace = _workspace(workspace, ws, q.device)
     if out.dim() != 3 or tuple(out.shape) != (T, hq, D) or out.dtype != q.dtype or out.device != q.device:
         raise ValueError(f"out must be a {q.dtype} [T, hq, D] = {(T, hq, D)} tensor on {q.device}")
     _expect(lse, "lse", (hq, T), torch.float32, q.device)
@@ -428,8 +442,7 @@ def varlen_attn_bwd_rope(q_rot, k_rot, v, out, dout, lse, cu_seqlens, max_seqlen
         dq = torch.empty(T, hq, D, **g) if dq is None else dq
         dk = torch.empty(T, hkv, D, **g) if dk is None else dk
         dv = torch.empty(T, hkv, D, **g) if dv is None else dv
-        if workspace is None or workspace.numel() < ws:
-            workspace = torch.empty(max(ws, 256), dtype=torch.uint8, device=q_rot.device)
+        workspace = _workspace(workspace, ws, q_rot.device)
     _expect(dq, "dq", (T, hq, D), gtype, q_rot.device)
     _expect(dk, "dk", (T, hkv, D), gtype, q_rot.device)
     _expect(dv, "dv", (T, hkv, D), gtype, q_rot.device)

@@ -180,6 +180,9 @@ def test_debug_library_reports_its_checks():
     assert psc.lib().psc_varlen_attn_workspace(0, psc.BF16, 4096, 8, 1024, 8, 2, 128, ctypes.byref(b_rel)) == 0
     assert D.psc_varlen_attn_workspace(0, psc.BF16, 4096, 8, 1024, 8, 2, 128, ctypes.byref(b_dbg)) == 0
     assert b_dbg.value == b_rel.value + 256
+    # and the binding's sizing call asks the library it is given
+    assert psc.varlen_attn_workspace(1, psc.BF16, 4096, 8, 1024, 8, 2, 128, library=D) == \
+        psc.varlen_attn_workspace(1, psc.BF16, 4096, 8, 1024, 8, 2, 128) + 256
 
 
 @pytest.mark.parametrize("cu,n,T,flags", [(None, 3, 16, 16), (16, 3, 16, None), (16, -1, 16, 16),
@@ -219,6 +222,20 @@ def test_binding_rejects_mismatched_buffers_before_the_call():
         psc.varlen_attn_bwd(q, k, k, q, q, lse, cu, T, dq=torch.zeros(T, hq, D, **g32),
                             dk=torch.zeros(T, hkv, D, **g32), dv=torch.zeros(T, hkv, D, **g32),
                             grad_dtype=psc.BF16)
+    # a caller's workspace is checked, never replaced
+    ws = psc.varlen_attn_workspace(0, psc.BF16, T, 1, T, hq, hkv, D)
+    wb = psc.varlen_attn_workspace(1, psc.BF16, T, 1, T, hq, hkv, D)
+    with pytest.raises(ValueError, match="needs"):  # one byte short
+        psc.varlen_attn_fwd(q, k, k, cu, T, out=q.clone(), lse=lse, workspace=torch.zeros(ws - 1, dtype=torch.uint8))
+    with pytest.raises(ValueError, match="uint8"):  # not bytes
+        psc.varlen_attn_fwd(q, k, k, cu, T, out=q.clone(), lse=lse, workspace=torch.zeros(ws, dtype=torch.int32))
+    with pytest.raises(ValueError, match="contiguous"):  # strided
+        psc.varlen_attn_fwd(q, k, k, cu, T, out=q.clone(), lse=lse,
+                            workspace=torch.zeros(2 * ws, dtype=torch.uint8)[::2])
+    with pytest.raises(ValueError, match="needs"):
+        psc.varlen_attn_bwd(q, k, k, q, q, lse, cu, T, dq=torch.zeros(T, hq, D, **g32),
+                            dk=torch.zeros(T, hkv, D, **g32), dv=torch.zeros(T, hkv, D, **g32),
+                            workspace=torch.zeros(wb - 1, dtype=torch.uint8))
 
 
 def test_attn_workspace_sizes():
