@@ -13,7 +13,9 @@
  *    and no output is touched.  A failed launch returns PSC_ERR_HIP.
  *  - The library allocates no device memory.  The caller owns every buffer,
  *    including the scratch `workspace`, whose size comes from the matching
- *    *_workspace / *_sizes call.  No pointer is kept after a call returns.
+ *    *_workspace / *_sizes call and whose address must be 16-byte aligned
+ *    (PSC_ERR_WORKSPACE when it is null or short, PSC_ERR_INVALID when it is
+ *    misaligned).  No pointer is kept after a call returns.
  *  - Calls are reentrant; two calls that share an output or a workspace buffer
  *    must not overlap in time.
  *  - No C++ exception crosses this interface.

@@ -86,6 +86,15 @@ size_t rope_table_bytes(const psc::AttnDims& d) {
 size_t attn_part(int pass, int dtype, const psc::AttnDims& d) {
   return pass % 2 == 0 ? psc::attn_fwd_workspace_bytes(dtype, d) : psc::attn_bwd_workspace_bytes(dtype, d);
 }
+// A caller's workspace: PSC_ERR_WORKSPACE when missing or shorter than
+// `need`, PSC_ERR_INVALID when not 16-byte aligned (the kernels read the
+// schedule entries carved from it as 16-byte vectors).
+int workspace_status(const void* ws, size_t bytes, size_t need) {
+  if (!ws || bytes < need) return PSC_ERR_WORKSPACE;
+  if (reinterpret_cast<uintptr_t>(ws) % 16 != 0) return PSC_ERR_INVALID;
+  return PSC_OK;
+}
+
 size_t workspace_for(int pass, int dtype, const psc::AttnDims& d) {
   return attn_part(pass, dtype, d) + (pass >= 2 ? rope_table_bytes(d) : 0) + kDebugTail;
 }
@@ -307,7 +316,7 @@ int psc_pack_build(int mode, const int32_t* tokens, const int64_t* doc_offsets, 
   if (n_docs == 0 && n_tokens != 0) return PSC_ERR_INVALID;
   if (max_segments < segs) return PSC_ERR_CAPACITY;
   const size_t need = psc::pack_workspace_bytes(n_docs, rows);
-  if (!workspace || workspace_bytes < need) return PSC_ERR_WORKSPACE;
+  if (int c = workspace_status(workspace, workspace_bytes, need)) return c;
 
   psc::PackArgs a;
   a.mode = mode;
@@ -352,7 +361,8 @@ int psc_varlen_attn_fwd(int dtype, const void* q, const void* k, const void* v, 
   if (st != PSC_OK) return st;
   const int64_t T = total_tokens;
   const size_t need = workspace_for(0, dtype, d);
-  if (T > 0 && (!workspace || workspace_bytes < need)) return PSC_ERR_WORKSPACE;
+  if (T > 0)
+    if (int c = workspace_status(workspace, workspace_bytes, need)) return c;
   if (T == 0) return PSC_OK;
   return fwd_launch(dtype, d, q, k, v, q_tok_stride, k_tok_stride, v_tok_stride, cu_seqlens, out, out_tok_stride,
                     lse, workspace, need, static_cast<hipStream_t>(stream));
@@ -391,7 +401,8 @@ int psc_varlen_attn_bwd(int dtype, int grad_dtype, const void* q, const void* k,
                       head_dim, softmax_scale, dq, dk, dv, &d);
   if (st != PSC_OK) return st;
   const size_t need = workspace_for(1, dtype, d);
-  if (total_tokens > 0 && (!workspace || workspace_bytes < need)) return PSC_ERR_WORKSPACE;
+  if (total_tokens > 0)
+    if (int c = workspace_status(workspace, workspace_bytes, need)) return c;
   if (total_tokens == 0) return PSC_OK;
   return bwd_launch(dtype, grad_dtype, d, q, k, v, out, dout, lse, q_tok_stride, k_tok_stride, v_tok_stride,
                     out_tok_stride, dout_tok_stride, cu_seqlens, dq, dk, dv, workspace, need,
@@ -412,7 +423,8 @@ int psc_varlen_attn_fwd_rope(int dtype, void* q, void* k, const void* v, int64_t
   if (st != PSC_OK) return st;
   const int64_t T = total_tokens;
   const size_t need = workspace_for(2, dtype, d);
-  if (T > 0 && (!workspace || workspace_bytes < need)) return PSC_ERR_WORKSPACE;
+  if (T > 0)
+    if (int c = workspace_status(workspace, workspace_bytes, need)) return c;
   if (T == 0) return PSC_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
 #ifdef PSC_DEBUG_CHECKS
@@ -457,7 +469,8 @@ int psc_varlen_attn_bwd_rope(int dtype, int grad_dtype, const void* q_rot, const
   st = rope_checks(dtype, head_dim, positions, rope_base, total_tokens);
   if (st != PSC_OK) return st;
   const size_t need = workspace_for(3, dtype, d);
-  if (total_tokens > 0 && (!workspace || workspace_bytes < need)) return PSC_ERR_WORKSPACE;
+  if (total_tokens > 0)
+    if (int c = workspace_status(workspace, workspace_bytes, need)) return c;
   if (total_tokens == 0) return PSC_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
 #ifdef PSC_DEBUG_CHECKS

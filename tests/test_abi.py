@@ -119,6 +119,27 @@ def test_attn_fwd_rejects_on_host(kw, code):
     assert _fwd_raw(**kw) == code
 
 
+# The cases below pass fake device pointers that are otherwise valid, so only
+# the check under test stands between them and a launch: they run only where
+# no GPU driver is present (a missing check then shows as PSC_ERR_HIP).
+no_gpu_driver = pytest.mark.skipif(os.path.exists("/dev/kfd"),
+                                   reason="launch-capable fake pointers: run on hosts without a GPU only")
+
+
+@no_gpu_driver
+def test_misaligned_workspace_is_rejected():
+    assert _fwd_raw(ws=24) == psc.ERR_INVALID
+    assert _pack_build_raw(ws=24) == psc.ERR_INVALID
+    v = lambda x: None if x is None else ctypes.c_void_p(x)
+    bwd = [psc.BF16, psc.F32, v(16), v(16), v(16), v(16), v(16), v(16), 256, 128, 128, 256, 256, v(16), 1, 16, 16,
+           2, 1, 128, 0.0, v(16), v(16), v(16), v(24), 1 << 24, None]
+    assert psc.lib().psc_varlen_attn_bwd(*bwd) == psc.ERR_INVALID
+    assert _rope_fwd_raw(ws=24, wsb=1 << 24) == psc.ERR_INVALID
+    bwd_rope = [psc.BF16, psc.F32, v(16), v(16), v(16), v(16), v(16), v(16), 256, 128, 128, 256, 256, v(16), 1, 16,
+                16, 2, 1, 128, v(16), 10000.0, 0.0, v(16), v(16), v(16), v(24), 1 << 24, None]
+    assert psc.lib().psc_varlen_attn_bwd_rope(*bwd_rope) == psc.ERR_INVALID
+
+
 def test_attn_empty_is_a_no_op():
     assert _fwd_raw(T=0, nseg=0, maxlen=0, q=None, k=None, v=None, out=None, lse=None, cu=None, ws=None) == 0
 
