@@ -1,11 +1,15 @@
 // Document-causal attention in true fp32 (no bf16 or tf32 rounding anywhere).
 //
-// Small-problem path for fp32 inputs: one thread per (query row, head) for the
-// forward and dQ, one thread per (key row, key/value head) for dK/dV.  Scores,
+// Path for fp32 inputs.  Each (query row, head) of the forward and dQ, and
+// each (key row, key/value head) of dK/dV, belongs to a group of 16 lanes of
+// one wave: lane r of the group holds elements r E .. r E + E - 1 (E = D/16)
+// of the row's vectors, a dot product is a per-lane partial sum reduced over
+// the group, and a thread holds only E elements of any vector.  Scores,
 // softmax and products are fp32 FMA; exp and log are the full-precision
-// library functions.  Each thread visits only its own document's causal range
-// ("Sample Packing：长序列 LLM 训练的 Attention 问题及优化", section 三: one causal
-// triangle per document), so the cost is the in-document work, without tiles.
+// library functions.  Each group visits only
+// its own document's causal range ("Sample Packing：长序列 LLM 训练的 Attention
+// 问题及优化", section 三: one causal triangle per document), so the cost is
+// the in-document work, without tiles.
 #include <cmath>
 
 #include "psc_internal.h"
@@ -13,7 +17,9 @@
 namespace psc {
 namespace {
 
-constexpr int kThreads = 128;
+constexpr int kThreads = 256;
+constexpr int kGroup = 16;                  // lanes per row
+constexpr int kRows = kThreads / kGroup;   // rows per workgroup
 
 // Segment holding token t: last s with cu[s] <= t.
 __device__ inline int32_t seg_of(const int32_t* cu, int32_t n_seg, int64_t t) {
@@ -25,6 +31,13 @@ __device__ inline int32_t seg_of(const int32_t* cu, int32_t n_seg, int64_t t) {
   return lo;
 }
 
+// Sum over the 16 lanes of a group (xor butterfly inside 16-lane rows).
+__device__ __forceinline__ float group_sum(float x) {
+#pragma unroll
+  for (int m = kGroup / 2; m >= 1; m >>= 1) x += __shfl_xor(x, m, kGroup);
+  return x;
+}
+
 struct F32Params {
   const float *q, *k, *v, *o, *dout, *lse_in;
   float *out, *lse, *Dbuf, *dq, *dk, *dv;
@@ -34,138 +47,166 @@ struct F32Params {
   float scale;
 };
 
+// E = D / 16 consecutive elements of a row, from lane r's slice.
+template <int E>
+__device__ __forceinline__ void load_slice(const float* row, int r, float (&x)[E]) {
+#pragma unroll
+  for (int e = 0; e < E; ++e) x[e] = row[r * E + e];
+}
+
 template <int D>
 __global__ void __launch_bounds__(kThreads) k_f32_fwd(F32Params p) {
-  const int64_t t = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  constexpr int E = D / kGroup;
+  const int r = threadIdx.x % kGroup;
+  const int64_t t = (int64_t)blockIdx.x * kRows + threadIdx.x / kGroup;
   const int32_t head = blockIdx.y;
-  if (t >= p.T) return;
+  if (t >= p.T) return;  // whole groups leave together
   const int32_t s = seg_of(p.cu, p.n_seg, t);
   const int64_t s0 = min(max((int64_t)p.cu[s], (int64_t)0), t);
   const int32_t g = head / p.group;
-  float qv[D], acc[D];
-  const float* qr = p.q + t * p.sq + (int64_t)head * D;
-  for (int d = 0; d < D; ++d) {
-    qv[d] = qr[d];
-    acc[d] = 0.f;
-  }
+  float qv[E], acc[E];
+  load_slice<E>(p.q + t * p.sq + (int64_t)head * D, r, qv);
+#pragma unroll
+  for (int e = 0; e < E; ++e) acc[e] = 0.f;
   float m = -INFINITY, l = 0.f;
   for (int64_t j = s0; j <= t; ++j) {
-    const float* kr = p.k + j * p.sk + (int64_t)g * D;
+    float kv[E], vv[E];
+    load_slice<E>(p.k + j * p.sk + (int64_t)g * D, r, kv);
+    load_slice<E>(p.v + j * p.sv + (int64_t)g * D, r, vv);
     float x = 0.f;
-    for (int d = 0; d < D; ++d) x = fmaf(qv[d], kr[d], x);
-    x *= p.scale;
+#pragma unroll
+    for (int e = 0; e < E; ++e) x = fmaf(qv[e], kv[e], x);
+    x = group_sum(x) * p.scale;
     const float mn = fmaxf(m, x);
     const float a = expf(m - mn);
-    const float e = expf(x - mn);
-    l = l * a + e;
-    const float* vr = p.v + j * p.sv + (int64_t)g * D;
-    for (int d = 0; d < D; ++d) acc[d] = fmaf(e, vr[d], acc[d] * a);
+    const float ex = expf(x - mn);
+    l = l * a + ex;
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[e] = fmaf(ex, vv[e], acc[e] * a);
     m = mn;
   }
   float* orow = p.out + t * p.so + (int64_t)head * D;
-  for (int d = 0; d < D; ++d) orow[d] = acc[d] / l;
-  p.lse[(int64_t)head * p.T + t] = m + logf(l);
+#pragma unroll
+  for (int e = 0; e < E; ++e) orow[r * E + e] = acc[e] / l;
+  if (r == 0) p.lse[(int64_t)head * p.T + t] = m + logf(l);
 }
 
 template <int D>
 __global__ void __launch_bounds__(kThreads) k_f32_pre(F32Params p) {
-  const int64_t t = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  constexpr int E = D / kGroup;
+  const int r = threadIdx.x % kGroup;
+  const int64_t t = (int64_t)blockIdx.x * kRows + threadIdx.x / kGroup;
   const int32_t head = blockIdx.y;
   if (t >= p.T) return;
-  const float* orow = p.o + t * p.so + (int64_t)head * D;
-  const float* drow = p.dout + t * p.sdo + (int64_t)head * D;
+  float ov[E], dv[E];
+  load_slice<E>(p.o + t * p.so + (int64_t)head * D, r, ov);
+  load_slice<E>(p.dout + t * p.sdo + (int64_t)head * D, r, dv);
   float acc = 0.f;
-  for (int d = 0; d < D; ++d) acc = fmaf(orow[d], drow[d], acc);
-  p.Dbuf[(int64_t)head * p.T + t] = acc;
+#pragma unroll
+  for (int e = 0; e < E; ++e) acc = fmaf(ov[e], dv[e], acc);
+  acc = group_sum(acc);
+  if (r == 0) p.Dbuf[(int64_t)head * p.T + t] = acc;
 }
 
 template <int D>
 __global__ void __launch_bounds__(kThreads) k_f32_dq(F32Params p) {
-  const int64_t t = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  constexpr int E = D / kGroup;
+  const int r = threadIdx.x % kGroup;
+  const int64_t t = (int64_t)blockIdx.x * kRows + threadIdx.x / kGroup;
   const int32_t head = blockIdx.y;
   if (t >= p.T) return;
   const int32_t s = seg_of(p.cu, p.n_seg, t);
   const int64_t s0 = min(max((int64_t)p.cu[s], (int64_t)0), t);
   const int32_t g = head / p.group;
-  float qv[D], dov[D], acc[D];
-  const float* qr = p.q + t * p.sq + (int64_t)head * D;
-  const float* dr = p.dout + t * p.sdo + (int64_t)head * D;
-  for (int d = 0; d < D; ++d) {
-    qv[d] = qr[d];
-    dov[d] = dr[d];
-    acc[d] = 0.f;
-  }
+  float qv[E], dov[E], acc[E];
+  load_slice<E>(p.q + t * p.sq + (int64_t)head * D, r, qv);
+  load_slice<E>(p.dout + t * p.sdo + (int64_t)head * D, r, dov);
+#pragma unroll
+  for (int e = 0; e < E; ++e) acc[e] = 0.f;
   const float lse = p.lse_in[(int64_t)head * p.T + t];
   const float Dt = p.Dbuf[(int64_t)head * p.T + t];
   for (int64_t j = s0; j <= t; ++j) {
-    const float* kr = p.k + j * p.sk + (int64_t)g * D;
-    const float* vr = p.v + j * p.sv + (int64_t)g * D;
+    float kv[E], vv[E];
+    load_slice<E>(p.k + j * p.sk + (int64_t)g * D, r, kv);
+    load_slice<E>(p.v + j * p.sv + (int64_t)g * D, r, vv);
     float x = 0.f, dp = 0.f;
-    for (int d = 0; d < D; ++d) {
-      x = fmaf(qv[d], kr[d], x);
-      dp = fmaf(dov[d], vr[d], dp);
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      x = fmaf(qv[e], kv[e], x);
+      dp = fmaf(dov[e], vv[e], dp);
     }
+    x = group_sum(x);
+    dp = group_sum(dp);
     const float pr = expf(x * p.scale - lse);
     const float ds = pr * (dp - Dt);
-    for (int d = 0; d < D; ++d) acc[d] = fmaf(ds, kr[d], acc[d]);
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[e] = fmaf(ds, kv[e], acc[e]);
   }
   float* out = p.dq + (t * p.hq + head) * D;
-  for (int d = 0; d < D; ++d) out[d] = acc[d] * p.scale;
+#pragma unroll
+  for (int e = 0; e < E; ++e) out[r * E + e] = acc[e] * p.scale;
 }
 
 template <int D>
 __global__ void __launch_bounds__(kThreads) k_f32_dkdv(F32Params p) {
-  const int64_t j = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  constexpr int E = D / kGroup;
+  const int r = threadIdx.x % kGroup;
+  const int64_t j = (int64_t)blockIdx.x * kRows + threadIdx.x / kGroup;
   const int32_t g = blockIdx.y;
   if (j >= p.T) return;
   const int32_t s = seg_of(p.cu, p.n_seg, j);
-  const int64_t e = min(max((int64_t)p.cu[s + 1], j + 1), p.T);
-  float kv[D], vv[D], dk[D], dv[D];
-  const float* kr = p.k + j * p.sk + (int64_t)g * D;
-  const float* vr = p.v + j * p.sv + (int64_t)g * D;
-  for (int d = 0; d < D; ++d) {
-    kv[d] = kr[d];
-    vv[d] = vr[d];
-    dk[d] = 0.f;
-    dv[d] = 0.f;
+  const int64_t e_end = min(max((int64_t)p.cu[s + 1], j + 1), p.T);
+  float kv[E], vv[E], dk[E], dv[E];
+  load_slice<E>(p.k + j * p.sk + (int64_t)g * D, r, kv);
+  load_slice<E>(p.v + j * p.sv + (int64_t)g * D, r, vv);
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    dk[e] = 0.f;
+    dv[e] = 0.f;
   }
   for (int32_t hh = 0; hh < p.group; ++hh) {
     const int32_t head = g * p.group + hh;
-    for (int64_t i = j; i < e; ++i) {
-      const float* qr = p.q + i * p.sq + (int64_t)head * D;
-      const float* dr = p.dout + i * p.sdo + (int64_t)head * D;
+    for (int64_t i = j; i < e_end; ++i) {
+      float qv[E], dov[E];
+      load_slice<E>(p.q + i * p.sq + (int64_t)head * D, r, qv);
+      load_slice<E>(p.dout + i * p.sdo + (int64_t)head * D, r, dov);
       float x = 0.f, dp = 0.f;
-      for (int d = 0; d < D; ++d) {
-        x = fmaf(qr[d], kv[d], x);
-        dp = fmaf(dr[d], vv[d], dp);
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        x = fmaf(qv[e], kv[e], x);
+        dp = fmaf(dov[e], vv[e], dp);
       }
+      x = group_sum(x);
+      dp = group_sum(dp);
       const float pr = expf(x * p.scale - p.lse_in[(int64_t)head * p.T + i]);
       const float ds = pr * (dp - p.Dbuf[(int64_t)head * p.T + i]);
-      for (int d = 0; d < D; ++d) {
-        dv[d] = fmaf(pr, dr[d], dv[d]);
-        dk[d] = fmaf(ds, qr[d], dk[d]);
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        dv[e] = fmaf(pr, dov[e], dv[e]);
+        dk[e] = fmaf(ds, qv[e], dk[e]);
       }
     }
   }
   float* dko = p.dk + (j * p.hkv + g) * D;
   float* dvo = p.dv + (j * p.hkv + g) * D;
-  for (int d = 0; d < D; ++d) {
-    dko[d] = dk[d] * p.scale;
-    dvo[d] = dv[d];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    dko[r * E + e] = dk[e] * p.scale;
+    dvo[r * E + e] = dv[e];
   }
 }
 
 template <int D>
 hipError_t fwd_d(const F32Params& p, hipStream_t st) {
-  dim3 grid((unsigned)((p.T + kThreads - 1) / kThreads), (unsigned)p.hq);
+  dim3 grid((unsigned)((p.T + kRows - 1) / kRows), (unsigned)p.hq);
   k_f32_fwd<D><<<grid, kThreads, 0, st>>>(p);
   return hipGetLastError();
 }
 
 template <int D>
 hipError_t bwd_d(const F32Params& p, hipStream_t st) {
-  dim3 gq((unsigned)((p.T + kThreads - 1) / kThreads), (unsigned)p.hq);
-  dim3 gk((unsigned)((p.T + kThreads - 1) / kThreads), (unsigned)p.hkv);
+  dim3 gq((unsigned)((p.T + kRows - 1) / kRows), (unsigned)p.hq);
+  dim3 gk((unsigned)((p.T + kRows - 1) / kRows), (unsigned)p.hkv);
   k_f32_pre<D><<<gq, kThreads, 0, st>>>(p);
   k_f32_dq<D><<<gq, kThreads, 0, st>>>(p);
   k_f32_dkdv<D><<<gk, kThreads, 0, st>>>(p);
