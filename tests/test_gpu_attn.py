@@ -302,12 +302,14 @@ def _layout(w):
     return np.asarray(pack_ref.flatten(rows, p.packed_length)["cu_seqlens"], dtype=np.int32)
 
 
-def sampled_check(q, k, v, do, cu, a_hq, a_hkv, dtype, backward, got, seed=1, head_kv=2):
+def sampled_check(q, k, v, do, cu, a_hq, a_hkv, dtype, backward, got, seed=1, head_kv=2, n_rows=192, n_tail=64,
+                  n_head_keys=128):
     """Sampled comparison with the oracle at full size.
 
-    O, lse and dQ: 192 random (row, head) pairs plus the last 64 rows of each
-    of the (up to 8) longest documents of at least 512 tokens, heads drawn at
-    random.  dK, dV: the first 128 keys of the longest document for `head_kv`
+    O, lse and dQ: n_rows (192) random (row, head) pairs plus the last n_tail
+    (64) rows of each of the (up to 8) longest documents of at least 512
+    tokens, heads drawn at random.  dK, dV: the first n_head_keys (128) keys of
+    the longest document for `head_kv`
     key/value heads (those keys sum over every later row of the document and
     every query head of the group: the most accumulated terms), its last 160
     keys for one head, and two whole short documents for every head."""
@@ -317,8 +319,8 @@ def sampled_check(q, k, v, do, cu, a_hq, a_hkv, dtype, backward, got, seed=1, he
     longest = int(np.argmax(lens))
     s_long, e_long = int(cu[longest]), int(cu[longest + 1])
     long_docs = [int(i) for i in np.argsort(-lens, kind="stable") if lens[i] >= 512][:8]
-    tails = [np.arange(int(cu[i + 1]) - 64, int(cu[i + 1])) for i in long_docs]
-    rows = np.concatenate([rng.integers(0, T, 192)] + tails)
+    tails = [np.arange(int(cu[i + 1]) - n_tail, int(cu[i + 1])) for i in long_docs]
+    rows = np.concatenate([rng.integers(0, T, n_rows)] + tails)
     heads = rng.integers(0, a_hq, rows.size)
     o, lse = attn_ref.attn_rows(q, k, v, cu, rows, heads)
     close("o", got["o"][rows, heads].float().numpy(), o, dtype)
@@ -328,12 +330,14 @@ def sampled_check(q, k, v, do, cu, a_hq, a_hkv, dtype, backward, got, seed=1, he
     dq = attn_ref.attn_rows_dq(q, k, v, do, cu, rows, heads)
     close(f"dq ({rows.size} rows)", got["dq"][rows, heads].numpy(), dq, dtype)
     kvs = sorted(int(g) for g in rng.choice(a_hkv, min(head_kv, a_hkv), replace=False))
-    key_hi = min(e_long, s_long + 128)
-    print(f"  dk/dv head keys [{s_long}, {key_hi}) of the {e_long - s_long}-token document, kv heads {kvs}",
-          flush=True)
-    dk, dv = attn_ref.attn_bwd_keys(q, k, v, do, cu, longest, s_long, kvs, key_hi=key_hi)
-    close("dk head", got["dk"][s_long:key_hi][:, kvs].numpy(), dk, dtype)
-    close("dv head", got["dv"][s_long:key_hi][:, kvs].numpy(), dv, dtype)
+    if n_head_keys > 0:
+        # the oracle needs lse and D of every row of the document for these
+        key_hi = min(e_long, s_long + n_head_keys)
+        print(f"  dk/dv head keys [{s_long}, {key_hi}) of the {e_long - s_long}-token document, kv heads {kvs}",
+              flush=True)
+        dk, dv = attn_ref.attn_bwd_keys(q, k, v, do, cu, longest, s_long, kvs, key_hi=key_hi)
+        close("dk head", got["dk"][s_long:key_hi][:, kvs].numpy(), dk, dtype)
+        close("dv head", got["dv"][s_long:key_hi][:, kvs].numpy(), dv, dtype)
     g = int(rng.integers(0, a_hkv))
     key_lo = max(s_long, e_long - 160)
     dk, dv = attn_ref.attn_bwd_keys(q, k, v, do, cu, longest, key_lo, [g])
@@ -364,6 +368,20 @@ def test_full_size_sampled(name, seed):
     print(f"[{name} seed {seed}] T={T} segments={len(cu) - 1} hq={a.hq} hkv={a.hkv} D={a.head_dim}", flush=True)
     got = run(q, k, v, do, cu, backward=a.backward)
     sampled_check(q, k, v, do, cu, a.hq, a.hkv, a.dtype, a.backward, got, head_kv=4 if a.hq == a.hkv else 2)
+
+
+def test_one_document_at_the_largest_size():
+    # one causal document over the whole 131072-token row (the 128K share's
+    # heads): the longest key walks any workload reaches, sampled
+    T = 131072
+    cu = np.array([0, T], dtype=np.int32)
+    q, k, v, do = workloads.qkv_do(T, 4, 1, 128, seed=2, dtype="bf16")
+    print(f"[one document] T={T}", flush=True)
+    got = run(q, k, v, do, cu)
+    # a lean sample (every sampled row spans up to 131072 keys); no head keys:
+    # their oracle needs every row of the document (O(T^2) in fp64), which the
+    # 2 x 32K and 128K-share workloads check on their longest documents
+    sampled_check(q, k, v, do, cu, 4, 1, "bf16", True, got, head_kv=1, n_rows=40, n_tail=16, n_head_keys=0)
 
 
 def test_full_size_repeat_is_bit_identical():
