@@ -4,7 +4,8 @@ Cases: the page's printed examples, every workload's document stream (the
 skewed one through the literal truncate-and-pad rule, 62 rows), and edge cases
 (a document ending exactly at a row end, a stream that fills its rows exactly,
 one-token documents, empty documents, a last truncate row with fewer than
-micro_bsz documents, no documents at all), plus random sweeps.
+micro_bsz documents, no documents at all), random sweeps, and one row of the
+largest length the ABI accepts (2^30 tokens).
 """
 import numpy as np
 import pytest
@@ -129,3 +130,39 @@ def test_repeat_is_identical():
     b = _gpu_pack(w.pack.docs, 1, 32768, psc.PACK)
     for key in ("ids", "labels", "indexes", "cu", "row_seg_ptr"):
         assert np.array_equal(a[key], b[key])
+
+
+@pytest.mark.parametrize("mode", [psc.PACK, psc.UNPACK])
+def test_row_of_the_largest_length(mode):
+    # one row of 2^30 tokens (the limit: rows x row length must fit cu_seqlens'
+    # int32): two documents, then 2^30 - 12 padding tokens.  The document part
+    # is compared with the oracle packing the same documents into a 28-token
+    # row; padding at sampled positions with its closed form (id 0, label
+    # -100, indexes counting from the end of the documents).
+    docs = [[11, 12, 13, 14, 15], [21, 22, 23, 24, 25, 26, 27]]
+    used = sum(len(d) for d in docs)
+    mb, sl = (1, 1 << 30) if mode == psc.PACK else (2, 1 << 29)
+    PL = mb * sl
+    toks = torch.tensor([t for d in docs for t in d], dtype=torch.int32).cuda()
+    offs = torch.tensor([0, 5, 12], dtype=torch.int64).cuda()
+    print(f"  packed row length {PL}, mode {mode}", flush=True)
+    r = psc.pack_build(toks, offs, mb, sl, mode)
+    torch.cuda.synchronize()
+    n_seg, max_seqlen, filled, flag = r["stats"].cpu().tolist()
+    assert (n_seg, max_seqlen, filled, flag) == (3, PL - used, 1, 0)
+    assert r["cu_seqlens"][:4].cpu().tolist() == [0, 5, used, PL]
+    assert r["row_seg_ptr"][:2].cpu().tolist() == [0, 3]
+    assert r["row_valid_len"][:1].cpu().tolist() == [used]
+    small_mb, small_sl = (1, 28) if mode == psc.PACK else (2, 14)
+    ref_rows = (pack_ref.build_pack if mode == psc.PACK else pack_ref.build_unpack)(docs, small_mb, small_sl)
+    f = pack_ref.flatten(ref_rows, 28)
+    head = 28
+    assert r["input_ids"][0, :head].cpu().tolist() == f["input_ids"]
+    assert r["labels"][0, :head].cpu().tolist() == f["labels"]
+    assert r["indexes"][0, :head].cpu().tolist() == f["indexes"]
+    rng = np.random.default_rng(5)
+    pos = np.concatenate([rng.integers(used, PL, 4096), [used, PL - 2, PL - 1]])
+    idx = torch.from_numpy(pos).cuda()
+    assert (r["input_ids"][0, idx] == 0).all()
+    assert (r["labels"][0, idx] == -100).all()
+    assert r["indexes"][0, idx].cpu().numpy().tolist() == (pos - used).tolist()
