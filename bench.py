@@ -13,10 +13,8 @@ segments are computed but not counted).  The default workload is the
 
 Prints one JSON line.  Besides the standard fields it carries
   roofline:     the dominant kernel's algorithmic FLOP rate (HIP events
-                recorded by the library around that kernel on its stream, over
-                a pass of the same number of steps run after the timed one, so
-                no instrumentation sits inside the timed region) against the
-                bf16 MFMA peak;
+                recorded by the library around that kernel on its stream,
+                summed over the timed steps) against the bf16 MFMA peak;
   cpu_baseline: the fp64 CPU oracle timed on a bounded sample of the same
                 workload (whole documents in order until ~--cpu-seconds of
                 work), in the same unit;
@@ -455,28 +453,30 @@ def measure(w, args, steps, warmup, torch, np, psc):
 
     for _ in range(warmup):
         step()
-    # 1. the timed region: `steps` steps with nothing recorded between them
+    # the timed region: events around each phase and the library's HIP events
+    # around each kernel on its stream (kernel breakdown, roofline)
+    torch.cuda.synchronize()
+    psc.timing_reset()
+    psc.timing_enable(True)
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0.record()
-    for _ in range(steps):
-        step()
-    t1.record()
-    torch.cuda.synchronize()
-    ms = t0.elapsed_time(t1) / steps
-    # 2. the same steps with events around each phase (forward / backward split)
     for i in range(steps):
         step(ev[i])
-    torch.cuda.synchronize()
-    # 3. and with the library's HIP events around each kernel (kernel breakdown,
-    # roofline); instrumentation stays out of the timed region above
-    psc.timing_reset()
-    psc.timing_enable(True)
-    for _ in range(steps):
-        step()
+    t1.record()
     torch.cuda.synchronize()
     psc.timing_enable(False)
     kt = psc.timing_read()
+    ms = t0.elapsed_time(t1) / steps
+    # the same number of steps once more with nothing recorded between them:
+    # what the instrumentation costs (reported beside, not as the value)
+    u0, u1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    u0.record()
+    for _ in range(steps):
+        step()
+    u1.record()
+    torch.cuda.synchronize()
+    ms_plain = u0.elapsed_time(u1) / steps
     fwd_all = [e[1].elapsed_time(e[2]) for e in ev]
     bwd_all = [e[2].elapsed_time(e[3]) for e in ev]
     fwd_ms = float(np.median(fwd_all))
@@ -487,6 +487,7 @@ def measure(w, args, steps, warmup, torch, np, psc):
         "hq": a.hq, "hkv": a.hkv, "head_dim": a.head_dim, "dtype": a.dtype,
         "passes": "pack+fwd+bwd" if a.backward else "pack+fwd", "steps": steps, "warmup": warmup,
         "ms_per_step": round(ms, 4), "tflops": round(value, 2),
+        "ms_per_step_uninstrumented": round(ms_plain, 4),
         "pct_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "tokens_per_s": round(real_tokens / (ms * 1e-3), 1),
         "pack_ms": round(float(np.median([e[0].elapsed_time(e[1]) for e in ev])), 4),
@@ -605,6 +606,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": summ["ms_per_step"],
+        "ms_per_step_uninstrumented": summ["ms_per_step_uninstrumented"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
