@@ -13,8 +13,10 @@ segments are computed but not counted).  The default workload is the
 
 Prints one JSON line.  Besides the standard fields it carries
   roofline:     the dominant kernel's algorithmic FLOP rate (HIP events
-                recorded by the library around that kernel on its stream,
-                summed over the timed steps) against the bf16 MFMA peak;
+                recorded by the library around that kernel alone on its
+                stream, summed over the timed steps; an untimed pass with every
+                kernel's events picks it and gives kernels_ms_per_step)
+                against the bf16 MFMA peak;
   cpu_baseline: the fp64 CPU oracle timed on a bounded sample of the same
                 workload (whole documents in order until ~--cpu-seconds of
                 work), in the same unit;
@@ -453,9 +455,27 @@ def measure(w, args, steps, warmup, torch, np, psc):
 
     for _ in range(warmup):
         step()
-    # the timed region: events around each phase and the library's HIP events
-    # around each kernel on its stream (kernel breakdown, roofline)
+    # untimed pass with the library's HIP events around every kernel: the
+    # kernel breakdown, and which attention kernel dominates the step
     torch.cuda.synchronize()
+    psc.timing_select(None)
+    psc.timing_reset()
+    psc.timing_enable(True)
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    psc.timing_enable(False)
+    kt = psc.timing_read()
+    algo = {"attn_fwd": fwd_flops}
+    if a.backward:
+        # forward = the two in-document products; dK/dV = S, dP, dV, dK (2.0x
+        # forward); dQ = the dQ product only (0.5x forward; the S and dP it
+        # recomputes are counted once, in dK/dV): the 2.5x convention
+        algo.update({"attn_bwd_dkdv": 2.0 * fwd_flops, "attn_bwd_dq": 0.5 * fwd_flops})
+    dom = max(algo, key=lambda n: kt[n][0])
+    # the timed region: events around each phase, and the library's HIP events
+    # around the dominant kernel alone (its launch durations for the roofline)
+    psc.timing_select([dom])
     psc.timing_reset()
     psc.timing_enable(True)
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -466,7 +486,8 @@ def measure(w, args, steps, warmup, torch, np, psc):
     t1.record()
     torch.cuda.synchronize()
     psc.timing_enable(False)
-    kt = psc.timing_read()
+    psc.timing_select(None)
+    kt_dom = psc.timing_read()[dom]
     ms = t0.elapsed_time(t1) / steps
     # the same number of steps once more with nothing recorded between them:
     # what the instrumentation costs (reported beside, not as the value)
@@ -502,7 +523,7 @@ def measure(w, args, steps, warmup, torch, np, psc):
                           "pct_peak": round(100 * bwd_flops / (bwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2)}
     ctx = dict(q=q, k=k, v=v, do=do, qd=qd, kd=kd, vd=vd, dod=dod, pk=pk, cu=cu, cu_h=cu_h, n_seg=n_seg,
                max_seqlen=max_seqlen, real=real, kt=kt, ms=ms, value=value, fwd_flops=fwd_flops,
-               bwd_flops=bwd_flops, step=step)
+               bwd_flops=bwd_flops, step=step, algo=algo, dom=dom, kt_dom=kt_dom)
     return summary, ctx
 
 
@@ -581,16 +602,10 @@ def main():
     w = workloads.make(args.workload, args.seed)
     a = w.attn
     summ, ctx = measure(w, args, args.steps, args.warmup, torch, np, psc)
-    kt, fwd_flops = ctx["kt"], ctx["fwd_flops"]
-
-    # dominant kernel and its algorithmic work per launch: forward = the two
-    # in-document products; dK/dV = S, dP, dV, dK (2.0x forward); dQ = the dQ
-    # product only (0.5x forward; the S and dP it recomputes are counted once,
-    # in dK/dV), so the backward kernels sum to the 2.5x convention.
-    algo = {"attn_fwd": fwd_flops, "attn_bwd_dkdv": 2.0 * fwd_flops if a.backward else 0.0,
-            "attn_bwd_dq": 0.5 * fwd_flops if a.backward else 0.0}
-    dom = max(algo, key=lambda n: kt[n][0])
-    dom_ms, dom_n = kt[dom]
+    # dominant kernel (from the untimed pass) and its algorithmic work per
+    # launch; its launch durations are the ones recorded in the timed region
+    algo, dom = ctx["algo"], ctx["dom"]
+    dom_ms, dom_n = ctx["kt_dom"]
     dom_avg = dom_ms / max(dom_n, 1)
     achieved = algo[dom] / (dom_avg * 1e-3) / 1e12
     roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,

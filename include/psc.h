@@ -385,6 +385,10 @@ int psc_debug_checks(void);
  * packer sequence counts as one "pack" launch).  psc_timing_read waits for the
  * recorded events and returns the summed elapsed time and launch count since
  * the last reset.  Host-side bookkeeping is thread safe; disabled by default.
+ * psc_timing_select limits the timed kernels to those whose bit (1 << k,
+ * k a psc_kernel) is set in kernel_mask (all of them by default, 0xFFFFFFFF),
+ * so a measurement can keep the events of one kernel alone in its timed
+ * region; it never fails.
  */
 typedef enum psc_kernel {
   PSC_K_PACK = 0,
@@ -398,6 +402,7 @@ typedef enum psc_kernel {
 } psc_kernel;
 
 int psc_timing_enable(int enable);
+int psc_timing_select(uint32_t kernel_mask);
 int psc_timing_reset(void);
 int psc_timing_read(int kernel, double* total_ms /* host out */, int64_t* launches /* host out */);
 const char* psc_kernel_name(int kernel);

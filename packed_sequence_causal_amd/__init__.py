@@ -18,7 +18,7 @@ Entry points (same names as the C ABI without the ``psc_`` prefix):
   rope                                    rotary embedding at the packer's indexes
   row_max_seqlen, unpack_data, split_sequence
                                           data steps after the packer
-  timing_enable, timing_reset, timing_read
+  timing_enable, timing_select, timing_reset, timing_read
                                           per-kernel HIP-event timing
 """
 from __future__ import annotations
@@ -55,6 +55,7 @@ _SIGNATURES = {
                                       ctypes.c_int32, ctypes.c_int64, _vp, _vp, _vp, _vp, ctypes.c_int64, _vp,
                                       _vp, _vp, _vp, ctypes.c_size_t, _vp]),
     "psc_timing_enable": (ctypes.c_int, [ctypes.c_int]),
+    "psc_timing_select": (ctypes.c_int, [ctypes.c_uint32]),
     "psc_timing_reset": (ctypes.c_int, []),
     "psc_timing_read": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(ctypes.c_double), _c_i64p]),
     "psc_kernel_name": (ctypes.c_char_p, [ctypes.c_int]),
@@ -555,6 +556,13 @@ KERNELS = {"pack": 0, "attn_schedule": 1, "attn_fwd": 2, "attn_bwd_pre": 3, "att
 
 def timing_enable(on: bool = True):
     _check(lib().psc_timing_enable(1 if on else 0), "psc_timing_enable")
+
+
+def timing_select(kernels=None):
+    """Time only the named kernels (names as in KERNELS) while timing is on;
+    None times every kernel."""
+    mask = 0xFFFFFFFF if kernels is None else sum(1 << KERNELS[k] for k in kernels)
+    _check(lib().psc_timing_select(mask), "psc_timing_select")
 
 
 def timing_reset():

@@ -18,6 +18,7 @@ struct Record {
 struct Timer {
   std::mutex mu;
   bool on = false;
+  uint32_t mask = ~0u;  // kernels timed while on (bit k = psc_kernel k)
   std::vector<Record> pending;
   std::vector<hipEvent_t> pool;
   double total_ms[kTimerSlots] = {};
@@ -63,7 +64,7 @@ int drain(Timer& t) {
 ScopedKernelTimer::ScopedKernelTimer(int slot, hipStream_t stream) : slot_(slot), stream_(stream) {
   Timer& t = timer();
   std::lock_guard<std::mutex> g(t.mu);
-  if (!t.on) return;
+  if (!t.on || slot < 0 || slot >= 32 || !((t.mask >> slot) & 1u)) return;
   start_ = take_event(t);
   if (start_ && hipEventRecord(static_cast<hipEvent_t>(start_), stream) != hipSuccess) start_ = nullptr;
 }
@@ -85,6 +86,13 @@ int psc_timing_enable(int enable) {
   psc::Timer& t = psc::timer();
   std::lock_guard<std::mutex> g(t.mu);
   t.on = enable != 0;
+  return PSC_OK;
+}
+
+int psc_timing_select(uint32_t kernel_mask) {
+  psc::Timer& t = psc::timer();
+  std::lock_guard<std::mutex> g(t.mu);
+  t.mask = kernel_mask;
   return PSC_OK;
 }
 

@@ -508,3 +508,35 @@ def test_debug_library_rejects_bad_cu_seqlens_before_launch():
         assert e.value.status == psc.ERR_INVALID
         torch.cuda.synchronize()
         assert torch.equal(out, sentinel)  # nothing was launched
+
+
+def test_kernel_timing_selects_kernels():
+    # psc_timing_select: only the selected kernels are bracketed by events
+    cu = np.concatenate([[0], np.cumsum(EDGE_LAYOUT)]).astype(np.int32)
+    T = int(cu[-1])
+    q, k, v, do = workloads.qkv_do(T, 8, 2, 128, seed=2, dtype="bf16")
+    dev = torch.device("cuda:0")
+    qd, kd, vd, cud = q.to(dev), k.to(dev), v.to(dev), torch.as_tensor(cu).to(dev)
+    try:
+        psc.timing_select(["attn_fwd"])
+        psc.timing_reset()
+        psc.timing_enable(True)
+        psc.varlen_attn_fwd(qd, kd, vd, cud, 431)
+        psc.varlen_attn_fwd(qd, kd, vd, cud, 431)
+        torch.cuda.synchronize()
+        psc.timing_enable(False)
+        kt = psc.timing_read()
+        assert kt["attn_fwd"][1] == 2 and kt["attn_fwd"][0] > 0
+        assert kt["attn_schedule"][1] == 0
+        psc.timing_select(None)
+        psc.timing_reset()
+        psc.timing_enable(True)
+        psc.varlen_attn_fwd(qd, kd, vd, cud, 431)
+        torch.cuda.synchronize()
+        psc.timing_enable(False)
+        kt = psc.timing_read()
+        assert kt["attn_fwd"][1] == 1 and kt["attn_schedule"][1] == 1
+    finally:
+        psc.timing_enable(False)
+        psc.timing_select(None)
+        psc.timing_reset()
