@@ -62,9 +62,9 @@ KERNEL_SOURCES = {
 }
 MEASURED_TRAFFIC = {
     # (kernel, workload): (sources sha256 prefix, read bytes, write bytes)
-    ("attn_fwd", "lognormal_32k"): ("2290f70f7c66f31f", 2.0 * 418320.5 * 1024, 1.0 * 533332.2 * 1024),
-    ("attn_bwd_dkdv", "lognormal_32k"): ("8ef2a2d29357273e", 2.0 * 4190203.7 * 1024, 1.0 * 532863.9 * 1024),
-    ("attn_bwd_dq", "lognormal_32k"): ("8ef2a2d29357273e", 2.0 * 965065.4 * 1024, 1.0 * 1066041.2 * 1024),
+    ("attn_fwd", "lognormal_32k"): ("2290f70f7c66f31f", 2.0 * 418581.0 * 1024, 1.0 * 533345.1 * 1024),
+    ("attn_bwd_dkdv", "lognormal_32k"): ("8ef2a2d29357273e", 2.0 * 4180083.1 * 1024, 1.0 * 532863.3 * 1024),
+    ("attn_bwd_dq", "lognormal_32k"): ("8ef2a2d29357273e", 2.0 * 964721.2 * 1024, 1.0 * 1066056.9 * 1024),
 }
 
 
