@@ -10,7 +10,7 @@ Source: InternEvo documentation, page "数据加载与流程" (data flow):
   * section "处理数据": packed_data_normalizer's max_seqlen, unpack_data and
     split_data_sequence_parallel (tp = 2 examples for packed and unpacked data).
 
-Readings taken where the page is silent (each is listed in the design doc):
+Readings taken where the page is silent:
   * labels are formed per whole document before a row split, so the last token
     of a row whose document continues gets the next document token as label;
   * a carried-over fragment at a row start is its own segment; a zero-padded

@@ -14,7 +14,7 @@ Sources:
   * "Sample Packing：长序列 LLM 训练的 Attention 问题及优化", section 4.1: with
     packed documents the position ids must restart per document as well.
 
-Reading (the pages print no formula; listed in the design doc): RoFormer's rotary
+Reading (the pages print no formula): RoFormer's rotary
 embedding in the rotate-half layout that an apply_rotary_pos_emb(q, k, cos,
 sin) call works on.  For head dimension D, dimensions i and i + D/2
 (0 <= i < D/2) form a pair that is rotated by the angle
